@@ -1,0 +1,314 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole hot path on one model shape (28 query heads,
+4 KV heads, head_dim 128): the causal GQA prefill of a 3314-token prompt (bf16)
+followed by a single-token split-KV decode against a 1641-token fp16 KV cache
+(split partials + LSE merge). Inputs are synthetic N(0,1) draws, resident in
+HBM before the timed region.
+
+Prints one JSON line. ``value`` is the prefill's algorithmic throughput in
+TFLOP/s (4 * head_dim FLOPs per visible query/key pair, per query head),
+timed with HIP events on the launch stream. The same line carries the
+decode timings, the batched long-context decode (32 sequences, 512..32768
+tokens) and the large-head prefill (head_dim 256, 8192 tokens) as extra
+measurements, a roofline entry per kernel family, and the fp64 CPU oracle's
+throughput on a bounded sample of the prefill workload.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_BF16_DENSE_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
+MI355X_HBM_GBPS = 8000.0
+
+
+def _dev(torch, bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16).cuda()
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def prefill_setup(torch, fa, cfg):
+    from flashattention_attention_amd import inputs
+    x = inputs.make_prefill_inputs(cfg)
+    q, k, v = (_dev(torch, x[n], cfg.dtype) for n in ("q", "k", "v"))
+    B, Sq, Hq, D = x["q"].shape
+    o = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    rs = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+
+    def run():
+        fa.prefill(q, k, v, causal=cfg.causal, softmax_scale=cfg.scale,
+                   out_unnormalized=cfg.out_unnormalized, out=o, lse=lse, row_sum=rs)
+    bytes_ = (q.numel() + k.numel() + v.numel()) * 2 + o.numel() * 4 + lse.numel() * 4 * (
+        2 if cfg.out_unnormalized else 1)
+    return run, bytes_
+
+
+def decode_setup(torch, fa, cfg, split_len=None):
+    from flashattention_attention_amd import inputs
+    x = inputs.make_decode_inputs(cfg)
+    q, kc, vc = (_dev(torch, x[n], cfg.dtype) for n in ("q", "k_cache", "v_cache"))
+    offs = torch.from_numpy(x["kv_offsets"]).cuda()
+    lens = torch.from_numpy(x["kv_lens"]).cuda()
+    if split_len is None:
+        split_len, max_splits = fa.decode_plan(cfg.batch, cfg.n_heads_kv, x["kv_lens"])
+    else:
+        max_splits = -(-int(x["kv_lens"].max()) // split_len)
+    B, Hq, D = x["q"].shape
+    po = torch.empty((B, Hq, max_splits, D), dtype=torch.float32, device="cuda")
+    pl = torch.empty((B, Hq, max_splits), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+
+    def partial():
+        fa.decode_split_partial(q, kc, vc, offs, lens, split_len=split_len,
+                                max_splits=max_splits, softmax_scale=cfg.scale, part_o=po,
+                                part_lse=pl)
+
+    def merge():
+        fa.decode_merge_lse(po, pl, lens, split_len=split_len, out=o, lse=lse)
+
+    kv_bytes = inputs.decode_kv_bytes(x["kv_lens"], cfg.n_heads_kv, cfg.head_dim)
+    alg_bytes = kv_bytes + q.numel() * 2 + o.numel() * 4 + lse.numel() * 4
+    n_parts = int(sum(-(-int(L) // split_len) for L in x["kv_lens"])) * Hq
+    part_bytes = 2 * n_parts * (D + 1) * 4           # written once, read once
+    return partial, merge, {"split_len": split_len, "max_splits": max_splits,
+                            "kv_bytes": kv_bytes, "alg_bytes": alg_bytes,
+                            "partial_bytes": part_bytes}
+
+
+def time_calls(torch, fns, iters, flush=None):
+    """Median / min per-call duration (ms) of each fn, HIP events on the current stream."""
+    per = [[] for _ in fns]
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        evs = _events(torch, len(fns) + 1)
+        evs[0].record()
+        for i, fn in enumerate(fns):
+            fn()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        for i in range(len(fns)):
+            per[i].append(evs[i].elapsed_time(evs[i + 1]))
+    return [{"median_ms": statistics.median(p), "min_ms": min(p), "mean_ms": statistics.mean(p)}
+            for p in per]
+
+
+def cpu_baseline(budget_s=20.0):
+    """fp64 oracle on a bounded sample of the prefill workload (rows spread over
+    the sequence, all heads), doubling the sample until ~budget_s of CPU work."""
+    import oracle
+    from flashattention_attention_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = inputs.GQA_PREFILL
+    x = inputs.make_prefill_inputs(cfg)
+    n, spent, last = 16, 0.0, None
+    while True:
+        rows = np.unique(np.linspace(0, cfg.seqlen_q - 1, n).astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=cfg.causal,
+                       dtype=cfg.dtype, rows=rows)
+        dt = time.perf_counter() - t0
+        spent += dt
+        off = cfg.seqlen_kv - cfg.seqlen_q
+        flops = 4 * cfg.head_dim * cfg.n_heads_q * cfg.batch * int(sum(r + off + 1 for r in rows))
+        last = (len(rows), dt, flops)
+        if spent >= budget_s / 2 or n >= cfg.seqlen_q:
+            break
+        n *= 2
+    nrows, dt, flops = last
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{nrows} query rows evenly spaced over the 3314-token prompt, all "
+                      f"{cfg.n_heads_q} heads, fp64 two-pass definition ({flops / 1e9:.2f} "
+                      f"GFLOP in {dt:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="also time the single-token decode at several split lengths")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from flashattention_attention_amd import fa, inputs
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    pcfg, dcfg = inputs.GQA_PREFILL, inputs.GQA_DECODE
+    print(f"[bench] {props.name} cus={props.multi_processor_count}; preparing inputs",
+          file=sys.stderr, flush=True)
+
+    prefill, _ = prefill_setup(torch, fa, pcfg)
+    d_partial, d_merge, dinfo = decode_setup(torch, fa, dcfg)
+
+    def step():
+        prefill()
+        d_partial()
+        d_merge()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [_events(torch, 4) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = evs[i]
+        e[0].record()
+        prefill()
+        e[1].record()
+        d_partial()
+        e[2].record()
+        d_merge()
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    part_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    pre_mean = statistics.mean(pre_ms)
+    flops = pcfg.flops()
+    value = flops / (pre_mean * 1e-3) / 1e12
+    dec_us = (statistics.mean(part_ms) + statistics.mean(merge_ms)) * 1e3
+    print(f"[bench] timed {K} steps: prefill {pre_mean * 1e3:.1f} us, decode "
+          f"{dec_us:.1f} us", file=sys.stderr, flush=True)
+
+    rooflines = {
+        "prefill_gqa_s3314": {"bound": "mfma", "achieved": round(value, 2),
+                              "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(value / MI355X_BF16_DENSE_TFLOPS, 4),
+                              "traffic": None,
+                              "kernel": "prefill_kernel<128,64,bf16>",
+                              "per_launch": f"{flops / 1e9:.2f} GFLOP"}}
+    line = {
+        "metric": "causal GQA prefill attention TFLOP/s (3314 tokens, 28/4 heads, hd 128, bf16)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{pcfg.name} + {dcfg.name}", "global_batch": 1,
+                   "seq_len": pcfg.seqlen_q, "kv_len_decode": 1641, "parallelism": "none"},
+        "prefill": {"us_per_call": round(pre_mean * 1e3, 2),
+                    "us_min": round(min(pre_ms) * 1e3, 2), "gflop": round(flops / 1e9, 3),
+                    "frac_mfma_peak": round(value / MI355X_BF16_DENSE_TFLOPS, 4)},
+        "decode_gqa_kv1641": {
+            "split_len": dinfo["split_len"], "max_splits": dinfo["max_splits"],
+            "us_per_call": round(dec_us, 2),
+            "partial_us": round(statistics.mean(part_ms) * 1e3, 2),
+            "merge_us": round(statistics.mean(merge_ms) * 1e3, 2),
+            "alg_gbps": round(dinfo["alg_bytes"] / (dec_us * 1e-6) / 1e9, 1),
+            "cache": "as left by the preceding prefill in the step"},
+    }
+
+    if not args.no_extras:
+        flush_buf = torch.empty(1 << 27, dtype=torch.float32, device="cuda")   # 512 MB
+
+        def flush():
+            flush_buf.zero_()
+
+        # single-token decode: cold (flushed) and hot
+        cold = time_calls(torch, [d_partial, d_merge], 20, flush=flush)
+        hot = time_calls(torch, [d_partial, d_merge], 50)
+        line["decode_gqa_kv1641"]["cold_us"] = round(
+            (cold[0]["median_ms"] + cold[1]["median_ms"]) * 1e3, 2)
+        line["decode_gqa_kv1641"]["hot_us"] = round(
+            (hot[0]["median_ms"] + hot[1]["median_ms"]) * 1e3, 2)
+        if args.split_sweep:
+            sweep = {}
+            for sl in (16, 32, 48, 64, 112, 208):
+                p2, m2, _ = decode_setup(torch, fa, dcfg, split_len=sl)
+                c = time_calls(torch, [p2, m2], 20, flush=flush)
+                sweep[sl] = round((c[0]["median_ms"] + c[1]["median_ms"]) * 1e3, 2)
+            line["decode_gqa_kv1641"]["cold_us_by_split_len"] = sweep
+        print("[bench] long decode", file=sys.stderr, flush=True)
+
+        lcfg = inputs.LONG_DECODE
+        l_partial, l_merge, linfo = decode_setup(torch, fa, lcfg)
+        for _ in range(3):
+            l_partial(); l_merge()
+        r = time_calls(torch, [l_partial, l_merge], 10, flush=flush)
+        tot_ms = r[0]["median_ms"] + r[1]["median_ms"]
+        part_gbps = (linfo["kv_bytes"] + 0.0) / (r[0]["median_ms"] * 1e-3) / 1e9
+        line["decode_batched_long"] = {
+            "workload": lcfg.name, "split_len": linfo["split_len"],
+            "max_splits": linfo["max_splits"], "kv_gb": round(linfo["kv_bytes"] / 1e9, 4),
+            "us_per_call": round(tot_ms * 1e3, 1),
+            "partial_us": round(r[0]["median_ms"] * 1e3, 1),
+            "merge_us": round(r[1]["median_ms"] * 1e3, 1),
+            "alg_gbps": round(linfo["alg_bytes"] / (tot_ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(linfo["alg_bytes"] / (tot_ms * 1e-3) / 1e9 / MI355X_HBM_GBPS,
+                                   4),
+            "partial_bytes_overhead_gb": round(linfo["partial_bytes"] / 1e9, 4),
+            "cache": "flushed (512 MB write) before every call"}
+        rooflines["decode_partial_batched_long"] = {
+            "bound": "hbm", "achieved": round(part_gbps, 1), "peak": MI355X_HBM_GBPS,
+            "unit": "GB/s", "frac": round(part_gbps / MI355X_HBM_GBPS, 4), "traffic": None,
+            "kernel": "decode_partial_kernel<128,4,f16>",
+            "per_launch": f"{linfo['kv_bytes'] / 1e9:.4f} GB of K+V"}
+        del l_partial, l_merge
+        torch.cuda.empty_cache()
+        print("[bench] large-head prefill", file=sys.stderr, flush=True)
+
+        hcfg = inputs.LARGE_HEAD
+        h_run, _ = prefill_setup(torch, fa, hcfg)
+        h_run()
+        r = time_calls(torch, [h_run], 5)
+        hf = hcfg.flops()
+        ht = hf / (r[0]["mean_ms"] * 1e-3) / 1e12
+        line["prefill_large_head"] = {"workload": hcfg.name,
+                                      "us_per_call": round(r[0]["mean_ms"] * 1e3, 1),
+                                      "tflops": round(ht, 2),
+                                      "frac_mfma_peak": round(ht / MI355X_BF16_DENSE_TFLOPS, 4)}
+        rooflines["prefill_large_head"] = {
+            "bound": "mfma", "achieved": round(ht, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ht / MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": None, "kernel": "prefill_kernel<256,32,bf16,unnormalized>",
+            "per_launch": f"{hf / 1e12:.4f} TFLOP"}
+        del flush_buf
+
+    line["roofline"] = rooflines["prefill_gqa_s3314"]
+    line["rooflines"] = rooflines
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

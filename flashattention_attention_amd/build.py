@@ -1,0 +1,65 @@
+"""Build libfa.so (gfx950 only) in-tree with hipcc.
+
+    python -m flashattention_attention_amd.build [--resource-usage]
+
+The library is written next to this file; the Python binding loads it from
+there. Every build compiles from scratch (a few tens of seconds).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libfa.so")
+SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def compile_flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            # packed-FP32 VALU ops stay disabled on purpose
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
+
+
+def build(resource_usage: bool = False, verbose: bool = False) -> str:
+    objs = []
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    tmpdir = os.path.join(PKG, "_build")
+    os.makedirs(tmpdir, exist_ok=True)
+    for src in SOURCES:
+        obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [hipcc()] + compile_flags() + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        if resource_usage or verbose:
+            sys.stdout.write(r.stderr)
+        objs.append(obj)
+    tmp_lib = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build(resource_usage="--resource-usage" in sys.argv, verbose="-v" in sys.argv)
+    print("built", path)

@@ -1,0 +1,192 @@
+// C-ABI entry points of libfa.so: argument validation (before any HIP call)
+// and dispatch to the gfx950 kernel launchers. See include/fa.h for the
+// contract of each entry point.
+#include "../../include/fa.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool head_dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_UNKNOWN_STATUS";
+  }
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                   const void* k, int64_t k_sb, int64_t k_ss, int64_t k_sh,
+                   const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh,
+                   float* o, int64_t o_sb, int64_t o_ss, int64_t o_sh,
+                   float* lse, float* row_sum,
+                   int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                   int head_dim, int dtype, int causal, float softmax_scale,
+                   int out_unnormalized, void* stream) {
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: q, k, v, o and lse must be non-null");
+  if (out_unnormalized && !row_sum)
+    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: row_sum is required with out_unnormalized");
+  if (batch < 1 || seqlen_q < 1 || n_heads_q < 1 || n_heads_kv < 1)
+    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: batch, seqlen_q and head counts must be >= 1");
+  if (seqlen_kv < seqlen_q)
+    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: seqlen_kv (%d) < seqlen_q (%d)", seqlen_kv,
+                seqlen_q);
+  if (n_heads_q % n_heads_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: n_heads_q (%d) %% n_heads_kv (%d) != 0",
+                n_heads_q, n_heads_kv);
+  if (!head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: head_dim %d not in {64, 128, 256}", head_dim);
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: dtype %d is not FA_F16 or FA_BF16", dtype);
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: softmax_scale must be finite and > 0");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: q, k, v, o must be 16-byte aligned");
+  const int64_t hs[9] = {q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh};
+  for (int i = 0; i < 9; ++i)
+    if (hs[i] < 0 || hs[i] % 8 != 0)
+      return fail(FA_ERR_INVALID_ARG,
+                  "fa_prefill_fwd: q/k/v strides must be non-negative multiples of 8 elements");
+  if (o_sb < 0 || o_ss < 0 || o_sh < 0 || o_sb % 4 || o_ss % 4 || o_sh % 4)
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_prefill_fwd: o strides must be non-negative multiples of 4 elements");
+  if ((seqlen_q + 127) / 128 > 65535 || batch > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: grid too large (seqlen_q or batch)");
+
+  fa::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_sum = row_sum;
+  a.q_sb = q_sb; a.q_ss = q_ss; a.q_sh = q_sh;
+  a.k_sb = k_sb; a.k_ss = k_ss; a.k_sh = k_sh;
+  a.v_sb = v_sb; a.v_ss = v_ss; a.v_sh = v_sh;
+  a.o_sb = o_sb; a.o_ss = o_ss; a.o_sh = o_sh;
+  a.batch = batch; a.seqlen_q = seqlen_q; a.seqlen_kv = seqlen_kv;
+  a.n_heads_q = n_heads_q; a.n_heads_kv = n_heads_kv;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return hip_status(fa::launch_prefill(a, head_dim, dtype == FA_BF16, out_unnormalized != 0,
+                                       (hipStream_t)stream),
+                    "fa_prefill_fwd launch");
+}
+
+int fa_decode_plan(int batch, int n_heads_kv, int64_t total_kv_len, int max_kv_len,
+                   int num_cus, int* split_len_out, int* max_splits_out) {
+  if (!split_len_out || !max_splits_out)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: null output pointer");
+  if (batch < 1 || n_heads_kv < 1 || max_kv_len < 1 || num_cus < 1 ||
+      total_kv_len < max_kv_len || total_kv_len > (int64_t)batch * max_kv_len)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: inconsistent sizes");
+  // Aim for about 8 work items (one wave each) per compute unit, in splits
+  // of at least 32 keys and a multiple of 32, so that short caches still
+  // spread over many waves and long caches keep partial traffic small.
+  const int64_t target_items = (int64_t)num_cus * 8;
+  int64_t per = (total_kv_len * n_heads_kv + target_items - 1) / target_items;
+  int64_t split = ((per + 31) / 32) * 32;
+  if (split < 32) split = 32;
+  if (split > max_kv_len) split = ((int64_t)max_kv_len + 15) / 16 * 16;
+  *split_len_out = (int)split;
+  *max_splits_out = (int)(((int64_t)max_kv_len + split - 1) / split);
+  return ok();
+}
+
+int fa_decode_split_partial(const void* q, int64_t q_sb, int64_t q_sh,
+                            const void* k_cache, const void* v_cache,
+                            int64_t kv_stride_tok, int64_t kv_stride_head,
+                            const int64_t* kv_offsets, const int32_t* kv_lens,
+                            int batch, int n_heads_q, int n_heads_kv, int head_dim, int dtype,
+                            float softmax_scale, int split_len, int max_splits,
+                            float* part_o, float* part_lse, void* stream) {
+  if (!q || !k_cache || !v_cache || !kv_offsets || !kv_lens || !part_o || !part_lse)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_split_partial: null pointer argument");
+  if (batch < 1 || n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_split_partial: bad batch or head counts");
+  if (!head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_split_partial: head_dim %d not in {64, 128, 256}",
+                head_dim);
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_split_partial: unsupported dtype %d", dtype);
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_split_partial: softmax_scale must be finite and > 0");
+  if (split_len < 16 || split_len % 16 != 0 || max_splits < 1)
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_decode_split_partial: split_len must be a positive multiple of 16, "
+                "max_splits >= 1");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o))
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_split_partial: misaligned pointer");
+  if (q_sb < 0 || q_sh < 0 || kv_stride_tok < 0 || kv_stride_head < 0 || q_sb % 8 ||
+      q_sh % 8 || kv_stride_tok % 8 || kv_stride_head % 8)
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_decode_split_partial: strides must be non-negative multiples of 8");
+  if (max_splits > 2147483647 / 2 || batch > 65535 || n_heads_q > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_split_partial: grid too large");
+
+  fa::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.kv_offsets = kv_offsets; a.kv_lens = kv_lens;
+  a.part_o = part_o; a.part_lse = part_lse;
+  a.q_sb = q_sb; a.q_sh = q_sh; a.kv_st = kv_stride_tok; a.kv_sh = kv_stride_head;
+  a.batch = batch; a.n_heads_q = n_heads_q; a.n_heads_kv = n_heads_kv;
+  a.split_len = split_len; a.max_splits = max_splits;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return hip_status(fa::launch_decode_partial(a, head_dim, dtype == FA_BF16, (hipStream_t)stream),
+                    "fa_decode_split_partial launch");
+}
+
+int fa_decode_merge_lse(const float* part_o, const float* part_lse, const int32_t* kv_lens,
+                        int batch, int n_heads_q, int head_dim, int split_len, int max_splits,
+                        float* o, float* lse, void* stream) {
+  if (!part_o || !part_lse || !kv_lens || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_merge_lse: null pointer argument");
+  if (batch < 1 || n_heads_q < 1 || split_len < 1 || max_splits < 1)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_merge_lse: sizes must be >= 1");
+  if (!head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_merge_lse: head_dim %d not in {64, 128, 256}",
+                head_dim);
+  if (batch > 65535 || n_heads_q > 2147483647 / 2)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_merge_lse: grid too large");
+  fa::MergeArgs a;
+  a.part_o = part_o; a.part_lse = part_lse; a.kv_lens = kv_lens; a.o = o; a.lse = lse;
+  a.batch = batch; a.n_heads_q = n_heads_q; a.split_len = split_len; a.max_splits = max_splits;
+  return hip_status(fa::launch_decode_merge(a, head_dim, (hipStream_t)stream),
+                    "fa_decode_merge_lse launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal declarations shared by the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Arguments of one prefill launch (element strides; head_dim stride is 1).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  float* row_sum;  // may be null in normalized mode
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv;
+  int causal;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int64_t* kv_offsets;
+  const int32_t* kv_lens;
+  float* part_o;
+  float* part_lse;
+  int64_t q_sb, q_sh;
+  int64_t kv_st, kv_sh;
+  int batch, n_heads_q, n_heads_kv;
+  int split_len, max_splits;
+  float scale_log2;
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* kv_lens;
+  float* o;
+  float* lse;
+  int batch, n_heads_q, split_len, max_splits;
+};
+
+// Launchers: enqueue on `stream`, return the launch's hipError_t.
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, bool unnormalized,
+                          hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
+                                 hipStream_t stream);
+hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,260 @@
+"""Python binding of libfa.so (argument marshalling only).
+
+Each function here takes torch tensors that live on an AMD GPU, checks the
+shapes and devices, allocates outputs with torch when the caller did not pass
+them, and calls the C ABI declared in ``include/fa.h`` on torch's current
+HIP stream. Every step of the attention computation runs in the library's
+HIP kernels; there is no fallback path. If the library is missing, or a
+tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "fa.h")
+_lib = None
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F16, FA_BF16 = 0, 1
+
+_i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+_SIGNATURES = {
+    "fa_prefill_fwd": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                        _vp, _i64, _i64, _i64, _vp, _vp,
+                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp], _i32),
+    "fa_decode_plan": ([_i32, _i32, _i64, _i32, _i32, ctypes.POINTER(_i32),
+                        ctypes.POINTER(_i32)], _i32),
+    "fa_decode_split_partial": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
+                                 _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp],
+                                _i32),
+    "fa_decode_merge_lse": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
+    "fa_status_string": ([_i32], ctypes.c_char_p),
+    "fa_last_error": ([], ctypes.c_char_p),
+}
+
+
+class FAError(RuntimeError):
+    """A libfa call returned a non-OK status (or the library is unavailable)."""
+
+    def __init__(self, msg: str, status: int = -1):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libfa.so")
+
+
+def declared_functions() -> list:
+    """Names of the functions include/fa.h declares."""
+    text = open(_HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)
+
+
+def load_library():
+    """Load libfa.so (built in-tree) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FAError(f"{path} is not built; run `python -m flashattention_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != FA_OK:
+        lib = load_library()
+        raise FAError(f"{what}: {lib.fa_status_string(status).decode()}: "
+                      f"{lib.fa_last_error().decode()}", status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def _on_gpu(*tensors: torch.Tensor) -> torch.device:
+    dev = None
+    for t in tensors:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise FAError("every tensor argument must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise FAError("all tensors must be on the same GPU")
+    return dev
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True,
+            softmax_scale: Optional[float] = None, out_unnormalized: bool = False,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+            row_sum: Optional[torch.Tensor] = None, want_row_sum: bool = False):
+    """Attention forward. q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (fp16/bf16, D contiguous).
+
+    Returns (o, lse) or (o, lse, row_sum) when ``out_unnormalized`` or
+    ``want_row_sum``; o is fp32 [B,Sq,Hq,D] (un-normalized when asked), lse and
+    row_sum are fp32 [B,Hq,Sq].
+    """
+    dev = _on_gpu(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FAError("q, k, v must be 4-D [batch, seq, heads, head_dim]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FAError("q, k, v must share a dtype")
+    if k.shape != v.shape:
+        raise FAError("k and v must have the same shape")
+    for t in (q, k, v):
+        if t.stride(3) != 1:
+            raise FAError("head_dim must be the contiguous dimension")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise FAError("q and k disagree on batch or head_dim")
+    scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    need_rs = out_unnormalized or want_row_sum or row_sum is not None
+    if need_rs and row_sum is None:
+        row_sum = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    _on_gpu(out, lse, *([row_sum] if row_sum is not None else []))
+    if out.dtype != torch.float32 or out.shape != (B, Sq, Hq, D) or out.stride(3) != 1:
+        raise FAError("out must be fp32 [B,Sq,Hq,D] with contiguous head_dim")
+    for t in (lse, row_sum):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, Hq, Sq)
+                              or not t.is_contiguous()):
+            raise FAError("lse / row_sum must be contiguous fp32 [B,Hq,Sq]")
+    lib = load_library()
+    st = lib.fa_prefill_fwd(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+        v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
+        B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
+        1 if out_unnormalized else 0, _stream(dev))
+    _check(st, "fa_prefill_fwd")
+    return (out, lse, row_sum) if need_rs else (out, lse)
+
+
+def decode_plan(batch: int, n_heads_kv: int, kv_lens: Sequence[int],
+                num_cus: Optional[int] = None) -> Tuple[int, int]:
+    """Deterministic (split_len, max_splits) for host-known KV lengths."""
+    lens = [int(x) for x in kv_lens]
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    lib = load_library()
+    sl, ms = _i32(), _i32()
+    st = lib.fa_decode_plan(batch, n_heads_kv, sum(lens), max(lens), num_cus, ctypes.byref(sl),
+                            ctypes.byref(ms))
+    _check(st, "fa_decode_plan")
+    return sl.value, ms.value
+
+
+def decode_split_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         kv_offsets: torch.Tensor, kv_lens: torch.Tensor, *, split_len: int,
+                         max_splits: int, softmax_scale: Optional[float] = None,
+                         part_o: Optional[torch.Tensor] = None,
+                         part_lse: Optional[torch.Tensor] = None):
+    """Split partials. q [B,Hq,D]; caches [T,Hkv,D]; kv_offsets int64 [B]; kv_lens int32 [B].
+
+    Returns part_o fp32 [B,Hq,max_splits,D] and part_lse fp32 [B,Hq,max_splits]
+    (entries of empty splits are left untouched).
+    """
+    dev = _on_gpu(q, k_cache, v_cache, kv_offsets, kv_lens)
+    if q.dim() != 3 or k_cache.dim() != 3 or k_cache.shape != v_cache.shape:
+        raise FAError("q must be [B,Hq,D] and the caches [T,Hkv,D] of equal shape")
+    if k_cache.stride() != v_cache.stride():
+        raise FAError("k_cache and v_cache must share strides")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise FAError("q and the caches must share a dtype")
+    if kv_offsets.dtype != torch.int64 or kv_lens.dtype != torch.int32:
+        raise FAError("kv_offsets must be int64 and kv_lens int32")
+    if q.stride(2) != 1 or k_cache.stride(2) != 1:
+        raise FAError("head_dim must be contiguous")
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2] != D or kv_offsets.shape != (B,) or kv_lens.shape != (B,):
+        raise FAError("shape mismatch between q, caches, kv_offsets and kv_lens")
+    if not (kv_offsets.is_contiguous() and kv_lens.is_contiguous()):
+        raise FAError("kv_offsets and kv_lens must be contiguous")
+    scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
+    if part_o is None:
+        part_o = torch.empty((B, Hq, max_splits, D), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((B, Hq, max_splits), dtype=torch.float32, device=dev)
+    _on_gpu(part_o, part_lse)
+    if (part_o.shape != (B, Hq, max_splits, D) or not part_o.is_contiguous()
+            or part_o.dtype != torch.float32 or part_lse.shape != (B, Hq, max_splits)
+            or not part_lse.is_contiguous() or part_lse.dtype != torch.float32):
+        raise FAError("part_o / part_lse have the wrong shape, dtype or layout")
+    lib = load_library()
+    st = lib.fa_decode_split_partial(
+        q.data_ptr(), q.stride(0), q.stride(1), k_cache.data_ptr(), v_cache.data_ptr(),
+        k_cache.stride(0), k_cache.stride(1), kv_offsets.data_ptr(), kv_lens.data_ptr(),
+        B, Hq, Hkv, D, _dtype_code(q), scale, split_len, max_splits,
+        part_o.data_ptr(), part_lse.data_ptr(), _stream(dev))
+    _check(st, "fa_decode_split_partial")
+    return part_o, part_lse
+
+
+def decode_merge_lse(part_o: torch.Tensor, part_lse: torch.Tensor, kv_lens: torch.Tensor, *,
+                     split_len: int, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None):
+    """Merge partials by LSE. Returns o fp32 [B,Hq,D] and lse fp32 [B,Hq]."""
+    dev = _on_gpu(part_o, part_lse, kv_lens)
+    B, Hq, S, D = part_o.shape
+    if part_lse.shape != (B, Hq, S) or kv_lens.shape != (B,) or kv_lens.dtype != torch.int32:
+        raise FAError("part_lse / kv_lens shape mismatch")
+    if not (part_o.is_contiguous() and part_lse.is_contiguous() and kv_lens.is_contiguous()):
+        raise FAError("merge inputs must be contiguous")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _on_gpu(out, lse)
+    if out.shape != (B, Hq, D) or lse.shape != (B, Hq) or not out.is_contiguous() \
+            or not lse.is_contiguous():
+        raise FAError("out / lse shape mismatch")
+    lib = load_library()
+    st = lib.fa_decode_merge_lse(part_o.data_ptr(), part_lse.data_ptr(), kv_lens.data_ptr(),
+                                 B, Hq, D, split_len, S, out.data_ptr(), lse.data_ptr(),
+                                 _stream(dev))
+    _check(st, "fa_decode_merge_lse")
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, kv_offsets, kv_lens, *, split_len: int, max_splits: int,
+           softmax_scale: Optional[float] = None, part_o=None, part_lse=None, out=None,
+           lse=None):
+    """Split partials followed by the LSE merge (two launches on the current stream)."""
+    po, pl = decode_split_partial(q, k_cache, v_cache, kv_offsets, kv_lens, split_len=split_len,
+                                  max_splits=max_splits, softmax_scale=softmax_scale,
+                                  part_o=part_o, part_lse=part_lse)
+    return decode_merge_lse(po, pl, kv_lens, split_len=split_len, out=out, lse=lse)

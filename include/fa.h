@@ -1,0 +1,180 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) exact-attention library libfa.so.
+ *
+ * The library computes exact scaled-dot-product attention with a tiled online
+ * softmax on hand-written gfx950 HIP kernels:
+ *
+ *   - prefill: causal (or unmasked) GQA forward producing O and the per-row
+ *     log-sum-exp;
+ *   - decode: one query token per sequence against a KV cache, computed as
+ *     split-KV partials followed by a merge of the partials by their LSE.
+ *
+ * Definitions (all entry points):
+ *   s_ij = softmax_scale * sum_d q[i,d] * k[j,d]   for visible keys j
+ *   P_ij = exp(s_ij - m_i), m_i = max_j s_ij, l_i = sum_j P_ij (row sum)
+ *   O_i  = sum_j P_ij v[j,:] / l_i,   LSE_i = m_i + ln(l_i)   (natural log)
+ * Source: "STAGE_D.md — FMHA Kernel Development", section "Kernel Output"
+ * (un-normalized output, row sum and LSE; normalization outside the kernel is
+ * exact) and sections D3/D4 (a key is masked iff its index exceeds the query
+ * position). Query head h reads KV head h / (n_heads_q / n_heads_kv): the
+ * KV-head addressing of "60 · r57 — FA KV staging double buffering
+ * (REVERTED)", section 2.2, with contiguous head groups.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller. The
+ *     library never allocates, frees or synchronizes; it only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL means the null stream).
+ *   - Half-precision inputs are fp16 or bf16 bit patterns (fa_dtype); all
+ *     arithmetic accumulates in fp32; every output is fp32.
+ *   - Strides are in ELEMENTS; the innermost (head_dim) stride is always 1.
+ *   - Arguments are validated on the host before any HIP call. A rejected
+ *     call returns FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED, enqueues
+ *     nothing, and leaves a description in fa_last_error(). A failed kernel
+ *     launch returns FA_ERR_HIP with the HIP error text.
+ *   - Results are deterministic: the same inputs and the same plan give the
+ *     same bytes on every run (no atomics; fixed reduction order).
+ *   - Thread-safe: no mutable global state besides the per-thread error text.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,  /* null pointer, bad size/stride/alignment, non-finite scale */
+  FA_ERR_UNSUPPORTED = 2,  /* valid request outside the supported set (head_dim, dtype) */
+  FA_ERR_HIP = 3           /* a HIP runtime call or kernel launch failed */
+} fa_status;
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * fa_prefill_fwd — attention forward over a whole prompt.
+ *
+ * Source: "STAGE_D.md — FMHA Kernel Development", "Kernel Output" (O, row
+ * sum, LSE; external normalization) and D3/D4 (mask comparator); "60 · r57 —
+ * FA KV staging double buffering (REVERTED)", sections 1 and 2.2 (grid over
+ * query block and head, KV tiles streamed up to the causal bound).
+ *
+ * Layouts (element strides, innermost dim contiguous):
+ *   q  [batch, seqlen_q,  n_heads_q,  head_dim]  half, strides q_sb, q_ss, q_sh
+ *   k  [batch, seqlen_kv, n_heads_kv, head_dim]  half, strides k_sb, k_ss, k_sh
+ *   v  [batch, seqlen_kv, n_heads_kv, head_dim]  half, strides v_sb, v_ss, v_sh
+ *   o  [batch, seqlen_q,  n_heads_q,  head_dim]  fp32, strides o_sb, o_ss, o_sh
+ *   lse     [batch, n_heads_q, seqlen_q] fp32, contiguous (natural-log LSE)
+ *   row_sum [batch, n_heads_q, seqlen_q] fp32, contiguous, or NULL
+ *
+ * causal != 0: query row i sits at position i + (seqlen_kv - seqlen_q)
+ * (bottom-right alignment) and sees keys j <= that position. causal == 0:
+ * every key is visible.
+ *
+ * out_unnormalized == 0: o = normalized output; row_sum (optional) = l_i.
+ * out_unnormalized != 0: o = sum_j P_ij v[j,:] with P_ij = exp(s_ij - m_i)
+ *   (m_i the row's true max), row_sum = l_i (required); the caller normalizes
+ *   o / row_sum.
+ *
+ * Supported set: head_dim in {64, 128, 256}; dtype FA_F16 or FA_BF16;
+ * n_heads_q % n_heads_kv == 0; 1 <= seqlen_q <= seqlen_kv; batch >= 1;
+ * softmax_scale finite and > 0; q/k/v/o base pointers 16-byte aligned; q/k/v
+ * stride_s, stride_h and stride_b multiples of 8, o strides multiples of 4.
+ * The inputs are read, never written; o/lse/row_sum are written in full.
+ */
+int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                   const void* k, int64_t k_sb, int64_t k_ss, int64_t k_sh,
+                   const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh,
+                   float* o, int64_t o_sb, int64_t o_ss, int64_t o_sh,
+                   float* lse, float* row_sum,
+                   int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                   int head_dim, int dtype, int causal, float softmax_scale,
+                   int out_unnormalized, void* stream);
+
+/*
+ * fa_decode_plan — deterministic split plan for split-KV decode (host only).
+ *
+ * Source: "66 · D2: explicit K+V register staging (LANDED, +2.0% @1641) and
+ * the cp.async negative result", section 1 (decode splits the KV length into
+ * ranges; the split count is part of the float summation order, so it must
+ * be a fixed function of the shape).
+ *
+ * Chooses split_len (keys per split, a multiple of 16) so that the
+ * (sequence, KV head, split) work items cover num_cus compute units several
+ * times over, and max_splits = ceil(max_kv_len / split_len). The result is a
+ * pure function of the arguments. Pass total_kv_len = sum of all sequence
+ * lengths. Returns FA_ERR_INVALID_ARG for non-positive sizes or null outputs.
+ */
+int fa_decode_plan(int batch, int n_heads_kv, int64_t total_kv_len, int max_kv_len,
+                   int num_cus, int* split_len_out, int* max_splits_out);
+
+/*
+ * fa_decode_split_partial — per-split partial attention for one query token.
+ *
+ * Source: "66 · D2 ...", sections 1 and 3.2 (each split [lo, hi) runs the
+ * online softmax over its KV rows with the K and V row loads issued ahead of
+ * the softmax dependency chain) and "STAGE_D.md ...", section D5 (partials
+ * carry an LSE so they can be merged).
+ *
+ * Layouts:
+ *   q        [batch, n_heads_q, head_dim] half, strides q_sb, q_sh
+ *   k_cache, v_cache: packed token-major caches; token t of sequence b, KV
+ *            head hk, element d at ((kv_offsets[b] + t) * kv_stride_tok +
+ *            hk * kv_stride_head + d)
+ *   kv_offsets [batch] int64, kv_lens [batch] int32 (device arrays, each
+ *            length >= 1)
+ *   part_o   [batch, n_heads_q, max_splits, head_dim] fp32, contiguous
+ *   part_lse [batch, n_heads_q, max_splits] fp32, contiguous
+ *
+ * Split s of sequence b covers keys [s*split_len, min(L_b, (s+1)*split_len));
+ * for s < ceil(L_b / split_len) it writes the normalized partial output O_s
+ * and its natural-log LSE_s. Splits at or past ceil(L_b / split_len) are
+ * empty: they are neither read nor written (their contents stay undefined).
+ * The caller guarantees ceil(L_b / split_len) <= max_splits (the merge writes
+ * NaN for any sequence that breaks this, and for L_b < 1).
+ *
+ * Supported set: head_dim in {64, 128, 256}; dtype FA_F16 or FA_BF16;
+ * n_heads_q % n_heads_kv == 0; split_len a positive multiple of 16;
+ * max_splits >= 1; pointers to half data 16-byte aligned, strides multiples
+ * of 8.
+ */
+int fa_decode_split_partial(const void* q, int64_t q_sb, int64_t q_sh,
+                            const void* k_cache, const void* v_cache,
+                            int64_t kv_stride_tok, int64_t kv_stride_head,
+                            const int64_t* kv_offsets, const int32_t* kv_lens,
+                            int batch, int n_heads_q, int n_heads_kv, int head_dim, int dtype,
+                            float softmax_scale, int split_len, int max_splits,
+                            float* part_o, float* part_lse, void* stream);
+
+/*
+ * fa_decode_merge_lse — merge split partials into the decode output.
+ *
+ * Source: "STAGE_D.md ...", section D5 (merging attention passes through
+ * their LSE) and "66 · D2 ...", section 5.2 (the combine step after the split
+ * partials). The merge formula is not printed on the pages; the max-shifted
+ * form is used: M = max_s LSE_s, w_s = exp(LSE_s - M),
+ * O = sum_s w_s O_s / sum_s w_s, LSE = M + ln(sum_s w_s).
+ *
+ * Reads only the first ceil(L_b / split_len) partials of sequence b.
+ * Layouts: part_o/part_lse as written by fa_decode_split_partial; o [batch,
+ * n_heads_q, head_dim] fp32 contiguous; lse [batch, n_heads_q] fp32. A
+ * sequence with L_b < 1 or ceil(L_b / split_len) > max_splits gets NaN in o
+ * and lse.
+ */
+int fa_decode_merge_lse(const float* part_o, const float* part_lse, const int32_t* kv_lens,
+                        int batch, int n_heads_q, int head_dim, int split_len, int max_splits,
+                        float* o, float* lse, void* stream);
+
+/* Static text for a status code. */
+const char* fa_status_string(int status);
+
+/* Detail for the last non-OK return on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

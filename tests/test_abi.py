@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/fa.h
+declares, plans deterministically, and rejects invalid arguments on the host
+before any HIP call (so nothing is ever launched here)."""
+import ctypes
+import os
+
+import pytest
+
+from flashattention_attention_amd import fa
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path()),
+                                reason="libfa.so not built")
+
+ALIGNED = 0x10000          # never dereferenced: every call below fails validation first
+
+
+def _gpu_visible():
+    # Counting devices does not initialise HIP on this image.
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+def test_exports_every_declared_symbol():
+    names = fa.declared_functions()
+    assert set(names) == {"fa_prefill_fwd", "fa_decode_plan", "fa_decode_split_partial",
+                          "fa_decode_merge_lse", "fa_status_string", "fa_last_error"}
+    lib = ctypes.CDLL(fa.library_path())
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = fa.load_library()
+    assert lib.fa_status_string(0) == b"FA_OK"
+    assert lib.fa_status_string(1) == b"FA_ERR_INVALID_ARG"
+    assert lib.fa_status_string(2) == b"FA_ERR_UNSUPPORTED"
+    assert lib.fa_status_string(3) == b"FA_ERR_HIP"
+
+
+def _plan(b, hkv, total, mx, cus=256):
+    lib = fa.load_library()
+    sl, ms = ctypes.c_int(), ctypes.c_int()
+    st = lib.fa_decode_plan(b, hkv, total, mx, cus, ctypes.byref(sl), ctypes.byref(ms))
+    return st, sl.value, ms.value
+
+
+def test_decode_plan_is_pure_and_covers_lengths():
+    for b, hkv, lens in [(1, 4, [1641]), (32, 8, [512 + 997 * i for i in range(32)]),
+                         (3, 2, [1, 29, 52]), (1, 1, [1])]:
+        st, sl, ms = _plan(b, hkv, sum(lens), max(lens))
+        assert st == 0
+        assert sl % 16 == 0 and sl >= 16
+        assert ms == -(-max(lens) // sl)
+        assert (st, sl, ms) == _plan(b, hkv, sum(lens), max(lens))
+
+
+@pytest.mark.parametrize("args", [
+    (0, 4, 10, 10, 256), (1, 0, 10, 10, 256), (1, 4, 10, 0, 256), (1, 4, 10, 10, 0),
+    (2, 4, 5, 10, 256),      # total < max
+    (2, 4, 25, 10, 256),     # total > batch * max
+])
+def test_decode_plan_rejects(args):
+    st, _, _ = _plan(*args)
+    assert st == fa.FA_ERR_INVALID_ARG
+
+
+def _prefill(**kw):
+    base = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED, row_sum=None,
+                B=1, Sq=128, Skv=128, Hq=4, Hkv=2, D=128, dtype=0, causal=1, scale=0.125,
+                unnorm=0, qs=(128 * 4 * 128, 4 * 128, 128), ks=(128 * 2 * 128, 2 * 128, 128),
+                os=(128 * 4 * 128, 4 * 128, 128))
+    base.update(kw)
+    b = base
+    lib = fa.load_library()
+    return lib.fa_prefill_fwd(b["q"], *b["qs"], b["k"], *b["ks"], b["v"], *b["ks"],
+                              b["o"], *b["os"], b["lse"], b["row_sum"], b["B"], b["Sq"],
+                              b["Skv"], b["Hq"], b["Hkv"], b["D"], b["dtype"], b["causal"],
+                              b["scale"], b["unnorm"], None)
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(unnorm=1), 1),
+    (dict(B=0), 1), (dict(Sq=0), 1), (dict(Skv=64), 1), (dict(Hkv=3), 1), (dict(Hq=0), 1),
+    (dict(D=96), 2), (dict(D=512), 2), (dict(dtype=7), 2),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=0.0), 1),
+    (dict(scale=-1.0), 1), (dict(q=ALIGNED + 2), 1), (dict(o=ALIGNED + 4), 1),
+    (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1), (dict(os=(128, 2, 128)), 1),
+    (dict(ks=(-8, 256, 128)), 1), (dict(Sq=70000 * 128, Skv=70000 * 128), 2),
+])
+def test_prefill_validation(kw, status):
+    st = _prefill(**kw)
+    assert st == status, fa.load_library().fa_last_error()
+    assert fa.load_library().fa_last_error() != b""
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lens=None), 1), (dict(Hkv=3), 1), (dict(D=80), 2),
+    (dict(dtype=2), 2), (dict(split=0), 1), (dict(split=24), 1), (dict(ms=0), 1),
+    (dict(scale=float("nan")), 1), (dict(k=ALIGNED + 8), 1), (dict(st=100), 1),
+])
+def test_decode_partial_validation(kw, status):
+    b = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, offs=ALIGNED, lens=ALIGNED, po=ALIGNED,
+             pl=ALIGNED, B=1, Hq=4, Hkv=2, D=128, dtype=0, scale=0.1, split=32, ms=4, st=256)
+    b.update(kw)
+    lib = fa.load_library()
+    st = lib.fa_decode_split_partial(b["q"], 512, 128, b["k"], b["v"], b["st"], 128, b["offs"],
+                                     b["lens"], b["B"], b["Hq"], b["Hkv"], b["D"], b["dtype"],
+                                     b["scale"], b["split"], b["ms"], b["po"], b["pl"], None)
+    assert st == status
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
+@pytest.mark.parametrize("kw,status", [
+    (dict(po=None), 1), (dict(o=None), 1), (dict(B=0), 1), (dict(split=0), 1), (dict(ms=0), 1),
+    (dict(D=100), 2),
+])
+def test_decode_merge_validation(kw, status):
+    b = dict(po=ALIGNED, pl=ALIGNED, lens=ALIGNED, o=ALIGNED, lse=ALIGNED, B=1, Hq=4, D=128,
+             split=32, ms=4)
+    b.update(kw)
+    lib = fa.load_library()
+    st = lib.fa_decode_merge_lse(b["po"], b["pl"], b["lens"], b["B"], b["Hq"], b["D"],
+                                 b["split"], b["ms"], b["o"], b["lse"], None)
+    assert st == status
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros((1, 8, 1, 64), dtype=torch.float16)
+    with pytest.raises(fa.FAError):
+        fa.prefill(q, q, q)

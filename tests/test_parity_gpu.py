@@ -1,0 +1,286 @@
+"""Parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Gate (from the method's statement of the problem): max |O_gpu - O_ref| <= 2e-3
+and max |LSE_gpu - LSE_ref| <= 1e-4 (natural log), element by element, for
+half-precision inputs with fp32 accumulation; outputs byte-identical run to
+run. Small problems are compared in full; the full-size workloads are compared
+on sampled rows (or sampled heads for decode) that the oracle computes one by
+one, in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from flashattention_attention_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-3
+LSE_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from flashattention_attention_amd import fa
+    fa.load_library()
+    return torch
+
+
+def _dev(torch, bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16).cuda()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _check_prefill(got_o, got_lse, ref, rows=None, got_rs=None, unnorm=False):
+    o = got_o if rows is None else got_o[:, rows]
+    lse = got_lse if rows is None else got_lse[:, :, rows]
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    if unnorm:
+        rs = got_rs if rows is None else got_rs[:, :, rows]
+        o = o / np.transpose(rs, (0, 2, 1))[..., None]
+        err_rs = np.abs(np.log(rs.astype(np.float64)) - np.log(ref["row_sum"])).max()
+        assert err_rs <= LSE_TOL, f"ln row_sum err {err_rs}"
+    err_o = np.abs(o - ref["o"]).max()
+    err_l = np.abs(lse - ref["lse"]).max()
+    assert err_o <= O_TOL and err_l <= LSE_TOL, f"O err {err_o:.3e}, LSE err {err_l:.3e}"
+    return err_o, err_l
+
+
+def _run_prefill(torch, fa_mod, q, k, v, dtype, causal, scale, unnorm=False, canary=True):
+    qd, kd, vd = _dev(torch, q, dtype), _dev(torch, k, dtype), _dev(torch, v, dtype)
+    B, Sq, Hq, D = q.shape
+    out = torch.full((B, Sq, Hq, D), float("nan"), device="cuda") if canary else None
+    lse = torch.full((B, Hq, Sq), float("nan"), device="cuda") if canary else None
+    rs = torch.full((B, Hq, Sq), float("nan"), device="cuda") if canary else None
+    res = fa_mod.prefill(qd, kd, vd, causal=causal, softmax_scale=scale,
+                         out_unnormalized=unnorm, out=out, lse=lse, row_sum=rs)
+    torch.cuda.synchronize()
+    return [r.cpu().numpy() for r in res]
+
+
+def test_tiny_workload_full(torch_gpu):
+    from flashattention_attention_amd import fa
+    cfg = inputs.TINY_CAUSAL
+    _say(cfg.name)
+    x = inputs.make_prefill_inputs(cfg)
+    ref = oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=True, dtype=cfg.dtype)
+    o, lse, rs = _run_prefill(torch_gpu, fa, x["q"], x["k"], x["v"], cfg.dtype, True, cfg.scale)
+    _check_prefill(o, lse, ref)
+    np.testing.assert_allclose(np.log(rs), np.log(ref["row_sum"]), atol=LSE_TOL, rtol=0)
+    # the first row sees one key: its output is that key's V row (up to the
+    # fp32 rounding of the exponent base, ~1 ulp of the row sum)
+    np.testing.assert_allclose(o[0, 0, 0], inputs.half_bits_to_f32(x["v"][0, 0, 0], cfg.dtype),
+                               rtol=1e-6, atol=1e-6)
+
+
+SWEEP = []
+for D in (64, 128, 256):
+    for S in (1, 2, 31, 33, 64, 65, 127, 129, 1000):
+        hq, hkv = (7, 1) if S % 2 else (8, 2)
+        SWEEP.append((1, S, S, hq, hkv, D, "bf16" if S % 3 else "f16", True, False))
+SWEEP += [
+    (2, 100, 300, 4, 4, 128, "bf16", True, False),    # Sq < Skv: bottom-right alignment
+    (1, 1, 777, 28, 4, 128, "f16", True, False),      # one query row against a long KV
+    (2, 200, 200, 6, 2, 64, "f16", False, False),     # unmasked
+    (1, 50, 333, 2, 1, 256, "bf16", False, False),    # unmasked, Sq < Skv
+    (2, 300, 300, 4, 2, 256, "bf16", True, True),     # un-normalized output
+    (1, 129, 129, 7, 7, 128, "bf16", True, True),
+    (3, 70, 70, 32, 8, 128, "f16", True, False),      # group 4, batch 3
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,D,dtype,causal,unnorm", SWEEP)
+def test_prefill_sweep(torch_gpu, B, Sq, Skv, Hq, Hkv, D, dtype, causal, unnorm):
+    from flashattention_attention_amd import fa
+    _say("prefill", B, Sq, Skv, Hq, Hkv, D, dtype, causal, unnorm)
+    rng = np.random.default_rng(Sq * 1000 + Skv + D)
+    q = inputs.draw_half(rng, (B, Sq, Hq, D), dtype)
+    k = inputs.draw_half(rng, (B, Skv, Hkv, D), dtype, mult=4.0 if unnorm else 1.0)
+    v = inputs.draw_half(rng, (B, Skv, Hkv, D), dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    ref = oracle.prefill(q, k, v, scale=scale, causal=causal, dtype=dtype)
+    res = _run_prefill(torch_gpu, fa, q, k, v, dtype, causal, scale, unnorm=unnorm)
+    _check_prefill(res[0], res[1], ref, got_rs=res[2], unnorm=unnorm)
+
+
+def test_prefill_strided_views(torch_gpu):
+    """q, k, v as views into one packed [B, S, Hq + 2 Hkv, D] tensor."""
+    from flashattention_attention_amd import fa
+    torch = torch_gpu
+    B, S, Hq, Hkv, D, dtype = 2, 190, 8, 2, 128, "bf16"
+    _say("strided", B, S, Hq, Hkv, D)
+    rng = np.random.default_rng(77)
+    qkv = inputs.draw_half(rng, (B, S, Hq + 2 * Hkv, D), dtype)
+    q, k, v = qkv[:, :, :Hq], qkv[:, :, Hq:Hq + Hkv], qkv[:, :, Hq + Hkv:]
+    scale = float(np.float32(1 / np.sqrt(D)))
+    ref = oracle.prefill(q, k, v, scale=scale, causal=True, dtype=dtype)
+    t = _dev(torch, qkv, dtype)
+    o, lse = fa.prefill(t[:, :, :Hq], t[:, :, Hq:Hq + Hkv], t[:, :, Hq + Hkv:], causal=True,
+                        softmax_scale=scale)
+    torch.cuda.synchronize()
+    _check_prefill(o.cpu().numpy(), lse.cpu().numpy(), ref)
+
+
+def _sample_rows(S, n_random, seed):
+    fixed = {0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, S // 2, S - 129, S - 128,
+             S - 65, S - 64, S - 2, S - 1}
+    rng = np.random.default_rng(seed)
+    fixed |= set(rng.integers(0, S, n_random).tolist())
+    return sorted(r for r in fixed if 0 <= r < S)
+
+
+def _full_size_prefill(torch, cfg, n_random):
+    from flashattention_attention_amd import fa
+    x = inputs.make_prefill_inputs(cfg)
+    runs = [_run_prefill(torch, fa, x["q"], x["k"], x["v"], cfg.dtype, cfg.causal, cfg.scale,
+                         unnorm=cfg.out_unnormalized) for _ in range(2)]
+    for a, b in zip(runs[0], runs[1]):                     # determinism: identical bytes
+        assert a.tobytes() == b.tobytes()
+    rows = _sample_rows(cfg.seqlen_q, n_random, cfg.seed)
+    ref = oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=cfg.causal,
+                         dtype=cfg.dtype, rows=rows)
+    o, lse, rs = runs[0]
+    assert np.isfinite(o).all() and np.isfinite(lse).all() and np.isfinite(rs).all()
+    return _check_prefill(o, lse, ref, rows=rows, got_rs=rs, unnorm=cfg.out_unnormalized)
+
+
+def test_gqa_prefill_full_size(torch_gpu):
+    _say(inputs.GQA_PREFILL.name)
+    _full_size_prefill(torch_gpu, inputs.GQA_PREFILL, 24)
+
+
+def test_large_head_prefill_full_size(torch_gpu):
+    _say(inputs.LARGE_HEAD.name)
+    _full_size_prefill(torch_gpu, inputs.LARGE_HEAD, 8)
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+
+def _dev_decode(torch, x, dtype):
+    return (_dev(torch, x["q"], dtype), _dev(torch, x["k_cache"], dtype),
+            _dev(torch, x["v_cache"], dtype), torch.from_numpy(x["kv_offsets"]).cuda(),
+            torch.from_numpy(x["kv_lens"]).cuda())
+
+
+def _decode_inputs_with_lens(lens, hq, hkv, D, dtype, seed):
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int32)
+    offs = np.concatenate([[0], np.cumsum(lens.astype(np.int64))[:-1]]).astype(np.int64)
+    T = int(lens.sum())
+    return {"q": inputs.draw_half(rng, (len(lens), hq, D), dtype),
+            "k_cache": inputs.draw_half(rng, (T, hkv, D), dtype),
+            "v_cache": inputs.draw_half(rng, (T, hkv, D), dtype),
+            "kv_lens": lens, "kv_offsets": offs}
+
+
+def _run_decode(torch, x, dtype, split_len, max_splits, scale):
+    from flashattention_attention_amd import fa
+    q, kc, vc, offs, lens = _dev_decode(torch, x, dtype)
+    B, Hq, D = x["q"].shape
+    po = torch.full((B, Hq, max_splits, D), float("nan"), device="cuda")
+    pl = torch.full((B, Hq, max_splits), float("nan"), device="cuda")
+    fa.decode_split_partial(q, kc, vc, offs, lens, split_len=split_len, max_splits=max_splits,
+                            softmax_scale=scale, part_o=po, part_lse=pl)
+    o, lse = fa.decode_merge_lse(po, pl, lens, split_len=split_len)
+    torch.cuda.synchronize()
+    return po.cpu().numpy(), pl.cpu().numpy(), o.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("split_len", ["plan", 16, 32, 48, 112, 208, 1648])
+def test_gqa_decode_workload(torch_gpu, split_len):
+    from flashattention_attention_amd import fa
+    cfg = inputs.GQA_DECODE
+    _say(cfg.name, split_len)
+    x = inputs.make_decode_inputs(cfg)
+    if split_len == "plan":
+        split_len, max_splits = fa.decode_plan(cfg.batch, cfg.n_heads_kv, x["kv_lens"])
+    else:
+        max_splits = -(-int(x["kv_lens"].max()) // split_len)
+    po, pl, o, lse = _run_decode(torch_gpu, x, cfg.dtype, split_len, max_splits, cfg.scale)
+    parts = oracle.decode_split_partials(x["q"], x["k_cache"], x["v_cache"], x["kv_offsets"],
+                                         x["kv_lens"], scale=cfg.scale, split_len=split_len,
+                                         max_splits=max_splits, dtype=cfg.dtype)
+    assert np.abs(po - parts["part_o"]).max() <= O_TOL
+    assert np.abs(pl - parts["part_lse"]).max() <= LSE_TOL
+    ref = oracle.decode(x["q"], x["k_cache"], x["v_cache"], x["kv_offsets"], x["kv_lens"],
+                        scale=cfg.scale, dtype=cfg.dtype)
+    assert np.abs(o - ref["o"]).max() <= O_TOL
+    assert np.abs(lse - ref["lse"]).max() <= LSE_TOL
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv", [("f16", 128, 28, 4), ("bf16", 128, 32, 8),
+                                            ("f16", 64, 8, 8), ("bf16", 256, 16, 2),
+                                            ("f16", 128, 12, 1)])
+def test_decode_lengths_and_empty_splits(torch_gpu, dtype, D, hq, hkv):
+    """KV lengths {1, 29, 52, 512, 1641} in one batch; room for empty splits that
+    must stay unwritten (their NaN canaries survive) and must not disturb the merge."""
+    _say("decode lens", dtype, D, hq, hkv)
+    lens = [1, 29, 52, 512, 1641]
+    x = _decode_inputs_with_lens(lens, hq, hkv, D, dtype, seed=D + hq)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    split_len = 48
+    max_splits = -(-max(lens) // split_len) + 3
+    po, pl, o, lse = _run_decode(torch_gpu, x, dtype, split_len, max_splits, scale)
+    for b, L in enumerate(lens):
+        ns = -(-L // split_len)
+        assert np.isnan(pl[b, :, ns:]).all() and np.isnan(po[b, :, ns:]).all()
+        assert np.isfinite(pl[b, :, :ns]).all()
+    ref = oracle.decode(x["q"], x["k_cache"], x["v_cache"], x["kv_offsets"], x["kv_lens"],
+                        scale=scale, dtype=dtype)
+    assert np.abs(o - ref["o"]).max() <= O_TOL
+    assert np.abs(lse - ref["lse"]).max() <= LSE_TOL
+    # one visible key: the output is that key's V row
+    hk_of = np.arange(hq) // (hq // hkv)
+    v0 = inputs.half_bits_to_f32(x["v_cache"][0], dtype)[hk_of]
+    np.testing.assert_allclose(o[0], v0, atol=1e-6, rtol=0)
+
+
+def test_decode_bad_lengths_give_nan(torch_gpu):
+    """A length needing more splits than max_splits, or zero, is reported as NaN."""
+    _say("decode bad lengths")
+    x = _decode_inputs_with_lens([64, 64, 64], 4, 2, 128, "f16", seed=5)
+    x["kv_lens"] = np.array([64, 0, 40], np.int32)
+    po, pl, o, lse = _run_decode(torch_gpu, x, "f16", 16, 3, 0.088)
+    assert np.isnan(o[0]).all() and np.isnan(lse[0]).all()     # 64 keys need 4 splits > 3
+    assert np.isnan(o[1]).all() and np.isnan(lse[1]).all()     # zero keys
+    assert np.isfinite(o[2]).all() and np.isfinite(lse[2]).all()
+
+
+def test_long_decode_full_size(torch_gpu):
+    from flashattention_attention_amd import fa
+    torch = torch_gpu
+    cfg = inputs.LONG_DECODE
+    _say(cfg.name)
+    x = inputs.make_decode_inputs(cfg)
+    split_len, max_splits = fa.decode_plan(cfg.batch, cfg.n_heads_kv, x["kv_lens"])
+    q, kc, vc, offs, lens = _dev_decode(torch, x, cfg.dtype)
+    outs = []
+    for _ in range(2):
+        o, lse = fa.decode(q, kc, vc, offs, lens, split_len=split_len, max_splits=max_splits,
+                           softmax_scale=cfg.scale)
+        torch.cuda.synchronize()
+        outs.append((o.cpu().numpy(), lse.cpu().numpy()))
+    assert outs[0][0].tobytes() == outs[1][0].tobytes()
+    assert outs[0][1].tobytes() == outs[1][1].tobytes()
+    o, lse = outs[0]
+    rng = np.random.default_rng(4)
+    picks = {(int(np.argmax(x["kv_lens"])), 0), (int(np.argmin(x["kv_lens"])), cfg.n_heads_q - 1)}
+    picks |= {(int(b), int(h)) for b, h in zip(rng.integers(0, cfg.batch, 14),
+                                                rng.integers(0, cfg.n_heads_q, 14))}
+    for b, h in sorted(picks):
+        sub = {"q": x["q"][b:b + 1, h:h + 1], "kv_lens": x["kv_lens"][b:b + 1],
+               "kv_offsets": x["kv_offsets"][b:b + 1]}
+        hk = h // (cfg.n_heads_q // cfg.n_heads_kv)
+        ref = oracle.decode(sub["q"], x["k_cache"][:, hk:hk + 1], x["v_cache"][:, hk:hk + 1],
+                            sub["kv_offsets"], sub["kv_lens"], scale=cfg.scale, dtype=cfg.dtype)
+        assert np.abs(o[b, h] - ref["o"][0, 0]).max() <= O_TOL, (b, h)
+        assert abs(lse[b, h] - ref["lse"][0, 0]) <= LSE_TOL, (b, h)
