@@ -145,6 +145,31 @@ def cpu_baseline(budget_s=20.0):
                       f"GFLOP in {dt:.2f} s)"}
 
 
+def run_profiling_aid(torch, fa, inputs, args):
+    """Single-component runs for rocprofv3 counter passes (no JSON contract line)."""
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        fns = [lambda: dst.copy_(src)]
+        label = f"copy {args.copy_bytes} bytes"
+    elif args.only in ("prefill", "large_head"):
+        cfg = inputs.GQA_PREFILL if args.only == "prefill" else inputs.LARGE_HEAD
+        run, _ = prefill_setup(torch, fa, cfg)
+        fns, label = [run], cfg.name
+    else:
+        cfg = inputs.GQA_DECODE if args.only == "decode" else inputs.LONG_DECODE
+        part, merge, _ = decode_setup(torch, fa, cfg)
+        fns, label = [part, merge], cfg.name
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    r = time_calls(torch, fns, args.steps)
+    print(f"[profiling aid] {label}: " + ", ".join(f"{x['mean_ms'] * 1e3:.2f} us" for x in r),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +179,11 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--split-sweep", action="store_true",
                     help="also time the single-token decode at several split lengths")
+    ap.add_argument("--only", choices=["prefill", "decode", "long_decode", "large_head"],
+                    help="profiling aid: run only this component (warmup + steps) and exit")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="profiling aid: time a plain device-to-device copy of this many "
+                         "bytes (the reference for scaling HBM traffic counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -168,6 +198,9 @@ def main():
     fa.load_library()
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
+    if args.copy_bytes or args.only:
+        run_profiling_aid(torch, fa, inputs, args)
+        return
     pcfg, dcfg = inputs.GQA_PREFILL, inputs.GQA_DECODE
     print(f"[bench] {props.name} cus={props.multi_processor_count}; preparing inputs",
           file=sys.stderr, flush=True)
