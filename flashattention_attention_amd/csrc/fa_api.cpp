@@ -61,7 +61,8 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                    float* lse, float* row_sum,
                    int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                    int head_dim, int dtype, int causal, float softmax_scale,
-                   int out_unnormalized, void* stream) {
+                   int out_unnormalized, void* workspace, uint64_t workspace_bytes,
+                   void* stream) {
   if (!q || !k || !v || !o || !lse)
     return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: q, k, v, o and lse must be non-null");
   if (out_unnormalized && !row_sum)
@@ -90,8 +91,15 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
   if (o_sb < 0 || o_ss < 0 || o_sh < 0 || o_sb % 4 || o_ss % 4 || o_sh % 4)
     return fail(FA_ERR_INVALID_ARG,
                 "fa_prefill_fwd: o strides must be non-negative multiples of 4 elements");
-  if ((seqlen_q + 127) / 128 > 65535 || batch > 65535)
+  if ((seqlen_q + 127) / 128 > 65535 || batch > 65535 || n_heads_q > 65535)
     return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: grid too large (seqlen_q or batch)");
+  if (k_ss > (int64_t)(1 << 23))
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: k sequence stride above 2^23 elements");
+  const uint64_t need = fa::prefill_workspace_bytes(batch, seqlen_kv, n_heads_kv, head_dim);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_prefill_fwd: workspace must be 256-byte aligned and hold %llu bytes",
+                (unsigned long long)need);
 
   fa::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_sum = row_sum;
@@ -103,9 +111,17 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
   a.n_heads_q = n_heads_q; a.n_heads_kv = n_heads_kv;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = softmax_scale * kLog2e;
-  return hip_status(fa::launch_prefill(a, head_dim, dtype == FA_BF16, out_unnormalized != 0,
+  fa::VtArgs w;
+  w.ws = workspace;
+  w.bytes = workspace_bytes;
+  return hip_status(fa::launch_prefill(a, w, head_dim, dtype == FA_BF16, out_unnormalized != 0,
                                        (hipStream_t)stream),
                     "fa_prefill_fwd launch");
+}
+
+uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int head_dim) {
+  if (batch < 1 || seqlen_kv < 1 || n_heads_kv < 1 || head_dim < 1) return 0;
+  return fa::prefill_workspace_bytes(batch, seqlen_kv, n_heads_kv, head_dim);
 }
 
 int fa_decode_plan(int batch, int n_heads_kv, int64_t total_kv_len, int max_kv_len,

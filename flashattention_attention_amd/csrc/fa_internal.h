@@ -47,9 +47,18 @@ struct MergeArgs {
   int batch, n_heads_q, split_len, max_splits;
 };
 
+// Caller-provided scratch for the prefill: fp16 V^T tiles.
+struct VtArgs {
+  void* ws;
+  size_t bytes;
+};
+
+// Bytes of prefill workspace needed for these sizes.
+size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int head_dim);
+
 // Launchers: enqueue on `stream`, return the launch's hipError_t.
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, bool unnormalized,
-                          hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
+                          bool unnormalized, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                                  hipStream_t stream);
 hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

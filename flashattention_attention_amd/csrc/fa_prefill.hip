@@ -1,48 +1,65 @@
 // Causal / unmasked GQA attention forward (prefill) for gfx950.
 //
-// One workgroup = 4 waves = 128 query rows of one (batch, query head); the
-// workgroup streams the K/V tiles of its KV head up to the causal bound and
-// keeps an online softmax per row.
+// Two launches on the caller's stream:
 //
-// Mapping to the CDNA4 matrix cores (v_mfma_f32_32x32x16_{bf16,f16}): every
-// wave owns 32 query rows and computes the TRANSPOSED score tile
-// S^T = K . Q^T, so the 32 queries run along the MFMA N dimension (one query
-// per lane column) and keys along M. With that orientation each lane holds
-// 16 keys of a single query row, so the row max and row sum are in-lane
-// reductions plus one exchange between the two 32-lane halves, and the
-// output O^T = V^T . P^T keeps one query per lane column as well, so the
-// per-row rescale is a per-lane scalar. P never leaves registers: the S^T
+//  1. vt_pack_kernel: V [B, Skv, Hkv, D] (fp16 or bf16) -> fp16 V^T tiles in
+//     the caller's workspace, laid out [B][Hkv][tile][D][64 keys], keys in
+//     the order the P.V
+//     contraction consumes them, 16-byte chunks XOR-swizzled inside every
+//     row, and zero-filled keys past Skv. bf16 V is converted to fp16 here, once, instead of in every
+//     work-group that reads the tile (exact for magnitudes in fp16's normal
+//     range).
+//
+//  2. prefill_kernel: one work-group = 8 waves filling one compute unit (2
+//     waves per SIMD) on one (batch, query head). At head_dim <= 128 each
+//     wave owns 32 query rows (256 per work-group) and takes whole 64-key
+//     tiles; at head_dim 256 waves w and w+4 own the same 32 rows (128 per
+//     work-group), each takes half of every tile with its own online softmax,
+//     and the pair is merged at the end.
+//
+// Mapping to the CDNA4 matrix cores (v_mfma_f32_32x32x16_{bf16,f16}): each
+// wave computes the TRANSPOSED score tile S^T = K . Q^T (keys along M, its 32
+// queries along N, one query per lane column), so the row max and row sum
+// are in-lane reductions plus one exchange between the two 32-lane halves,
+// and the output O^T = V^T . P^T keeps one query per lane column, so the
+// per-row rescale is a per-lane scalar. P stays in registers: the S^T
 // accumulator layout is reused as the B operand of the P.V contraction, with
 // the V^T A operand read from LDS in the matching key order.
 //
-// Tiling follows "60 · r57 — FA KV staging double buffering (REVERTED)",
-// sections 1 and 2.2 (grid over query block and head; KV tiles streamed to
-// the causal bound; tail rows zero-filled), with the softmax in registers of
-// its section 1 and the tile-end rescale of its section 2.3. K/V for tile t+1
-// are fetched into registers while tile t is computed (the overlap its
-// section 2.4 aims for), then written to LDS between two barriers.
+// K and V^T tiles move HBM -> LDS with direct global_load_lds_dwordx4 DMA
+// (no VGPR staging), into a two-stage LDS ring: the loads for tile t+1 are
+// issued before tile t is computed, and a single barrier per tile both
+// publishes tile t+1 and releases tile t's stage (the two fence duties of
+// the double-buffer scheme in "42 · r39 — q6_K KDR=2 double-buffer
+// (LANDED)", section 2.3). K rows are stored with a 16-byte-chunk XOR
+// swizzle so the 32-row MFMA operand reads hit distinct banks.
+//
+// Tiling and streaming follow "60 · r57 — FA KV staging double buffering
+// (REVERTED)", sections 1 and 2.2 (grid over query block and head; KV tiles
+// up to the causal bound; rows past the end never contribute), with the
+// softmax kept in registers (its section 1) and the tile-end rescale of its
+// section 2.3.
 //
 // Numerics:
 //  * scores accumulate in fp32 from exact half products; the softmax scale
 //    is applied to the fp32 scores (never folded into a half Q);
 //  * exponentials are base 2 on scores pre-multiplied by scale*log2(e);
-//  * P enters the P.V contraction as fp16 (round-to-nearest-even), V as fp16
-//    (bf16 V is converted; exact for magnitudes in fp16's normal range); a
-//    2^7 headroom factor keeps small P values out of fp16's subnormal range
-//    and cancels in O / l;
+//  * P enters P.V as fp16 (round-to-nearest-even) with a 2^7 headroom
+//    factor that keeps small P out of fp16's subnormal range and cancels in
+//    O / l; the row sum l accumulates the fp32 P values;
 //  * the running max is only moved (and O, l rescaled) once a tile max
-//    exceeds it by more than 2^8 — an exact identity, since O and l share
-//    the base — and outputs are referred back to the true row max;
-//  * the row sum l accumulates the fp32 P values.
+//    exceeds it by more than 2^8 — exact, since O and l share the base —
+//    and outputs are referred back to the true row max at the end.
 #include "fa_internal.h"
 
 #include <limits.h>
+
+#include <type_traits>
 
 namespace fa {
 namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -50,12 +67,25 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;          // query rows per workgroup
 constexpr float kShift = 7.0f;            // log2 of the fp16 headroom factor on P
 constexpr float kSlack = 8.0f;            // stale-max tolerance (log2 units)
 constexpr float kLn2 = 0.693147180559945309f;
+
+// Work-group geometry per head dim. key_split(d) = 1: eight groups of 32
+// query rows, each wave takes whole 64-key tiles (256 query rows per
+// work-group, so each K/V tile fetched serves 256 rows). key_split(d) = 2
+// (head_dim 256, where a wave cannot hold 64 keys of scores next to its Q and
+// O registers): waves w and w+4 own the same 32 query rows and each takes
+// half of every tile (128 query rows per work-group).
+__host__ __device__ constexpr int key_split(int d) { return d <= 128 ? 1 : 2; }
+__host__ __device__ constexpr int tile_keys(int d) {
+  return key_split(d) == 1 ? 64 : (d <= 128 ? 128 : 64);
+}
+__host__ __device__ constexpr int block_rows(int d) { return 32 * (8 / key_split(d)); }
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
@@ -79,33 +109,130 @@ __device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
 }
 
-// Packed bf16 pair -> packed fp16 pair.
-__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned w) {
-  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-}
-
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, int BN, bool BF16, bool UNNORM>
-__global__ void __launch_bounds__(kThreads)
-prefill_kernel(PrefillArgs a) {
-  constexpr int KSTR = D + 8;              // K tile row stride in LDS (elements)
-  constexpr int VSTR = BN + 4;             // V^T tile row stride in LDS (elements)
-  constexpr int NKK = D / 16;              // MFMA k-steps of Q.K^T
-  constexpr int NKB = BN / 32;             // 32-key blocks per tile
-  constexpr int NDB = D / 32;              // 32-row blocks of O^T
-  constexpr int NKS = BN / 16;             // MFMA k-steps of P.V
-  constexpr int KCH = BN * D / 8;          // 16-byte chunks in a K tile
-  constexpr int K_IT = (KCH + kThreads - 1) / kThreads;
-  constexpr int VUN = (BN / 4) * (D / 8);  // (4 keys x 8 dims) units in a V tile
-  constexpr int V_IT = (VUN + kThreads - 1) / kThreads;
+// The value of x held by lane (i ^ 32), combined with x by max or add: one
+// v_permlane32_swap exchanges the two 32-lane halves of a wave.
+__device__ __forceinline__ f32x2 halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const f32x2 v = halves(x);
+  return fmaxf(v[0], v[1]);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const f32x2 v = halves(x);
+  return v[0] + v[1];
+}
 
-  __shared__ __attribute__((aligned(16))) unsigned short k_lds[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) unsigned short vt_lds[D * VSTR];
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's bytes land at lds_addr + 16*i; lds_addr must be wave-uniform. Issued
+// through inline asm so that the compiler does not order the tile being
+// computed behind this prefetch; completion is awaited explicitly (dma_wait)
+// before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// V^T tile layout: D rows (head dims) x BN keys of fp16, BN*2 bytes per row
+// in 16-byte chunks. Chunk c holds keys 16*(c/2) + 4*(c%2) + {0,1,2,3} and
+// 16*(c/2) + 8 + 4*(c%2) + {0,1,2,3}: the key order in which the S^T
+// accumulator hands P to the P.V contraction, so one 16-byte read is one MFMA
+// operand. Chunks are XOR-swizzled by row so that the 32 rows read together
+// by an MFMA operand load fall on distinct banks.
+template <int BN>
+__device__ __forceinline__ int vt_chunk_offset(int d, int c) {
+  if constexpr (BN == 128) return d * 256 + ((c ^ (d & 15)) << 4);
+  else return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
+}
+
+// ---------------------------------------------------------------------------
+// V -> fp16 V^T tiles. One thread transposes 8 keys x 8 dims: the 8 keys of
+// one chunk (see vt_chunk_offset) for dims d0 .. d0+7.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ void __launch_bounds__(256)
+vt_pack_kernel(const unsigned short* __restrict__ v, int64_t v_sb, int64_t v_ss, int64_t v_sh,
+               int seqlen_kv, int n_heads_kv, int ntiles, unsigned short* __restrict__ ws) {
+  constexpr int BN = tile_keys(D);
+  constexpr int NCH = BN / 8;                        // chunks per V^T row
+  constexpr int UNITS = NCH * (D / 8);               // (chunk, dim-group) units per tile
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  const int t = u / UNITS;
+  if (t >= ntiles) return;
+  const int c = (u % UNITS) % NCH;                   // chunk: its 8 keys
+  const int d0 = ((u % UNITS) / NCH) * 8;            // dims d0 .. d0+7
+  const int hk = blockIdx.y, b = blockIdx.z;
+  const unsigned short* vp = v + (int64_t)b * v_sb + (int64_t)hk * v_sh + d0;
+  u32x4 row[8];                                      // row[j] = 8 dims of key j of the chunk
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int key = t * BN + 16 * (c / 2) + 4 * (c % 2) + (j & 3) + 8 * (j >> 2);
+    row[j] = key < seqlen_kv ? *(const u32x4*)(vp + (int64_t)key * v_ss) : u32x4{0, 0, 0, 0};
+    if (BF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        row[j][e] = pack_f16x2(__uint_as_float(row[j][e] << 16),
+                               __uint_as_float(row[j][e] & 0xffff0000u));
+    }
+  }
+  char* out = (char*)(ws + (((int64_t)b * n_heads_kv + hk) * ntiles + t) * (int64_t)(D * BN));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {                      // dims d0+2e (lo halves) and d0+2e+1 (hi)
+    u32x4 lo, hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = __builtin_amdgcn_perm(row[2 * j + 1][e], row[2 * j][e], 0x05040100u);
+      hi[j] = __builtin_amdgcn_perm(row[2 * j + 1][e], row[2 * j][e], 0x07060302u);
+    }
+    *(u32x4*)(out + vt_chunk_offset<BN>(d0 + 2 * e, c)) = lo;
+    *(u32x4*)(out + vt_chunk_offset<BN>(d0 + 2 * e + 1, c)) = hi;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention forward.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16, bool UNNORM>
+__global__ void __launch_bounds__(kThreads)
+prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
+  constexpr bool PIPE = D <= 128;            // software-pipelined loop (register budget)
+  constexpr int KS = key_split(D);           // waves sharing one query group
+  constexpr int QG = kWaves / KS;            // query groups of 32 rows
+  constexpr int kBM = 32 * QG;               // query rows per work-group
+  constexpr int BN = tile_keys(D);           // keys per tile
+  constexpr int KW = BN / KS;                // keys per wave per tile
+  constexpr int NKB = KW / 32;               // 32-key MFMA blocks per wave per tile
+  constexpr int NKS = KW / 16;               // MFMA k-steps of P.V per tile
+  constexpr int NKK = D / 16;                // MFMA k-steps of Q.K^T
+  constexpr int NDB = D / 32;                // 32-row blocks of O^T
+  constexpr int KROW = D * 2;                // bytes per K row
+  constexpr int KT = BN * KROW;              // bytes per K tile
+  constexpr int VT = D * BN * 2;             // bytes per V^T tile
+  constexpr int STAGE = KT + VT;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per K row
+  constexpr int RPI = 64 / CPR;              // K rows per 1 KB DMA instruction
+  constexpr int SWZ = CPR < 16 ? CPR - 1 : 15;
+  constexpr int K_INSTR = KT / 1024 / kWaves;   // DMA instructions per wave per tile
+  constexpr int V_INSTR = VT / 1024 / kWaves;
+  static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile too small for the DMA split");
+  static_assert(KS == 1 || 4 * NDB * 16 * 64 * 4 <= 2 * STAGE, "LDS too small for the pair merge");
+
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];   // K/V^T tiles, 2 of each
+  __shared__ float xs[KS == 2 ? 2 * 4 * 3 * 64 : 1];   // per-row softmax state, for the pair merge
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qw = wave % QG;       // which 32 query rows
+  const int kh = wave / QG;       // which part of every tile
   const int h = blockIdx.x;
   const int qb = (int)gridDim.y - 1 - (int)blockIdx.y;   // longest causal rows first
   const int b = blockIdx.z;
@@ -115,14 +242,9 @@ prefill_kernel(PrefillArgs a) {
 
   const int n = lane & 31;    // MFMA column = this lane's query within the wave
   const int hh = lane >> 5;   // lane half
-  const int qi = q0 + wave * 32 + n;
+  const int qi = q0 + qw * 32 + n;
   const bool q_valid = qi < a.seqlen_q;
   const int qpos = qi + off;
-
-  const unsigned short* kp =
-      (const unsigned short*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
-  const unsigned short* vp =
-      (const unsigned short*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
 
   // Q^T operand: 8 consecutive dims of this lane's query per k-step.
   u32x4 qr[NKK];
@@ -132,80 +254,72 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qr[kk] = q_valid ? *(const u32x4*)(qp + kk * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+    // Consume the Q registers here so the compiler waits for these loads now,
+    // and not at their first use inside the tile loop (where that wait would
+    // also stall on the prefetch DMA of the next tile).
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qr[kk]));
   }
 
   // KV range: keys up to the largest query position of the block.
   int kv_end = a.seqlen_kv;
   if (a.causal) kv_end = min(a.seqlen_kv, min(q0 + kBM, a.seqlen_q) + off);
   const int ntiles = (kv_end + BN - 1) / BN;
-  const int wave_first_qpos = q0 + wave * 32 + off;
-  const int wave_last_qpos =
-      a.causal ? min(q0 + wave * 32 + 31, a.seqlen_q - 1) + off : INT_MAX;
+  const int ntiles_all = (a.seqlen_kv + BN - 1) / BN;
+  const int wave_first_qpos = q0 + qw * 32 + off;
 
-  u32x4 kreg[K_IT];
-  u32x4 vreg[V_IT][4];
+  const unsigned short* kp =
+      (const unsigned short*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
+  const char* vtp = (const char*)vt_ws + ((int64_t)b * a.n_heads_kv + hk) * ntiles_all * VT;
 
-  auto load_tile = [&](int t0) {
+  // Per-lane element offsets of this wave's K DMA rows inside a tile (the
+  // host guarantees BN * k_ss fits in 32 bits).
+  int koff[K_INSTR];
 #pragma unroll
-    for (int i = 0; i < K_IT; ++i) {
-      const int c = tid + i * kThreads;
-      if (KCH % kThreads == 0 || c < KCH) {
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        const int key = t0 + row;
-        kreg[i] = key < a.seqlen_kv ? *(const u32x4*)(kp + (int64_t)key * a.k_ss + col)
-                                    : u32x4{0, 0, 0, 0};
+  for (int j = 0; j < K_INSTR; ++j) {
+    const int r = (wave * K_INSTR + j) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ (r & SWZ);
+    koff[j] = r * (int)a.k_ss + c * 8;
+  }
+  const unsigned lds_base = (unsigned)(uintptr_t)(lptr_t)lds;
+
+  // DMA of this wave's share of the K rows / V^T bytes of tile t to LDS offset dst.
+  auto issue_k = [&](int t, unsigned dst) {
+    const int t0 = t * BN;
+    const bool full = t0 + BN <= a.seqlen_kv;
+#pragma unroll
+    for (int j = 0; j < K_INSTR; ++j) {
+      const unsigned short* src;
+      if (full) {
+        src = kp + (int64_t)t0 * a.k_ss + koff[j];
+      } else {   // rows past the end repeat the last row; the mask zeroes them
+        const int r = (wave * K_INSTR + j) * RPI + lane / CPR;
+        const int key = min(t0 + r, a.seqlen_kv - 1);
+        src = kp + (int64_t)key * a.k_ss + (koff[j] - r * (int)a.k_ss);
       }
+      dma16(src, lds_base + dst + (wave * K_INSTR + j) * 1024);
     }
+  };
+  auto issue_v = [&](int t, unsigned dst) {
 #pragma unroll
-    for (int i = 0; i < V_IT; ++i) {
-      const int u = tid + i * kThreads;
-      if (VUN % kThreads == 0 || u < VUN) {
-        const int dc = u % (D / 8), kg = u / (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = t0 + kg * 4 + r;
-          vreg[i][r] = key < a.seqlen_kv
-                           ? *(const u32x4*)(vp + (int64_t)key * a.v_ss + dc * 8)
-                           : u32x4{0, 0, 0, 0};
-        }
-      }
+    for (int j = 0; j < V_INSTR; ++j) {
+      const int J = wave * V_INSTR + j;
+      dma16(vtp + (int64_t)t * VT + J * 1024 + lane * 16, lds_base + dst + J * 1024);
     }
   };
 
-  auto store_tile = [&]() {
+  // Loop-invariant LDS byte offsets of this lane's MFMA operands inside a stage.
+  // (The K swizzle repeats every 16 rows, so block kb adds a constant kb*32 rows.)
+  int ka_off[NKK];
 #pragma unroll
-    for (int i = 0; i < K_IT; ++i) {
-      const int c = tid + i * kThreads;
-      if (KCH % kThreads == 0 || c < KCH) {
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *(u32x4*)(k_lds + row * KSTR + col) = kreg[i];
-      }
-    }
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int r = kh * KW + n;
+    ka_off[kk] = r * KROW + (((2 * kk + hh) ^ (r & SWZ)) << 4);
+  }
+  int va_off[NKS];   // + db * 32 rows for head-dim block db (the swizzle repeats every 16 rows)
 #pragma unroll
-    for (int i = 0; i < V_IT; ++i) {
-      const int u = tid + i * kThreads;
-      if (VUN % kThreads == 0 || u < VUN) {
-        const int dc = u % (D / 8), kg = u / (D / 8);
-        u32x4 w[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[r][e] = BF16 ? bf16x2_to_f16x2(vreg[i][r][e]) : vreg[i][r][e];
-        }
-        // Transpose 4 keys x 8 dims into V^T rows: dim d gets keys kg*4 .. kg*4+3.
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u32x2 lo = {__builtin_amdgcn_perm(w[1][e], w[0][e], 0x05040100u),
-                      __builtin_amdgcn_perm(w[3][e], w[2][e], 0x05040100u)};
-          u32x2 hi = {__builtin_amdgcn_perm(w[1][e], w[0][e], 0x07060302u),
-                      __builtin_amdgcn_perm(w[3][e], w[2][e], 0x07060302u)};
-          *(u32x2*)(vt_lds + (dc * 8 + 2 * e) * VSTR + kg * 4) = lo;
-          *(u32x2*)(vt_lds + (dc * 8 + 2 * e + 1) * VSTR + kg * 4) = hi;
-        }
-      }
-    }
-  };
+  for (int ks = 0; ks < NKS; ++ks)
+    va_off[ks] = vt_chunk_offset<BN>(n, kh * (KW / 8) + ks * 2 + hh);
 
   float m_used = -1e30f;   // base of the exponentials (log2 units)
   float m_true = -1e30f;   // exact running row max (log2 units)
@@ -214,48 +328,37 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
-  if (ntiles > 0) load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = t * BN;
-    __syncthreads();                 // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();                 // the tile is complete in LDS
-    if (t + 1 < ntiles) load_tile(t0 + BN);
-    if (t0 > wave_last_qpos) continue;   // tile entirely above this wave's diagonal
-
-    // S^T = K . Q^T : rows = keys (M), columns = this wave's 32 queries (N).
-    f32x16 sacc[NKB];
+  // --- the phases of one tile for this wave --------------------------------
+  // S^T = K . Q^T : rows = this wave's keys (M, in blocks of 32), columns = its
+  // 32 queries (N). Independent accumulators per 32-key block.
+  auto qk = [&](const char* kst, f32x16 (&s)[NKB]) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 ka = *(const u32x4*)(k_lds + (kb * 32 + n) * KSTR + kk * 16 + hh * 8);
-        sacc[kb] = mfma_qk<BF16>(ka, qr[kk], sacc[kb]);
-      }
-    }
-
-    // Accumulator element i of block kb holds key t0 + kb*32 + (i/4)*8 + hh*4 + i%4.
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = mfma_qk<BF16>(*(const u32x4*)(kst + ka_off[kk] + kb * 32 * KROW), qr[kk], s[kb]);
+  };
+  // Mask, row max and (rarely) the move of the exponent base; returns the base.
+  // Element i of block kb holds key t0 + kb*32 + (i/4)*8 + hh*4 + i%4.
+  auto prep = [&](f32x16 (&s)[NKB], int t0) -> float {
     const bool need_mask =
-        (a.causal && t0 + BN - 1 > wave_first_qpos) || (t0 + BN > a.seqlen_kv);
+        (a.causal && t0 + KW - 1 > wave_first_qpos) || (t0 + KW > a.seqlen_kv);
     if (need_mask) {
+      const int lim = min(a.causal ? qpos : INT_MAX, a.seqlen_kv - 1) - t0 - hh * 4;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          const bool vis = key < a.seqlen_kv && (!a.causal || key <= qpos);
-          if (!vis) sacc[kb][i] = -INFINITY;
-        }
-      }
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kb][i] = -INFINITY;
     }
-
-    float mx = -INFINITY;
+    float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int i = (kb == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_halves(mx);
     const float tmax = mx * a.scale_log2;   // scale > 0: max commutes with the scaling
     m_true = fmaxf(m_true, tmax);
     const bool grow = tmax > m_used + kSlack;
@@ -269,47 +372,145 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
     }
-
-    // P = 2^(s*scale*log2e - (m_used - kShift)) <= 2^(kSlack + kShift) = 32768.
-    const float base = m_used - kShift;
-    u32x4 pk[NKS];
-    float ls = 0.0f;
+    return m_used - kShift;
+  };
+  // P = 2^(s*scale*log2e - base) <= 2^(kSlack + kShift) = 32768, packed to fp16.
+  auto expo = [&](const f32x16 (&s)[NKB], float base, u32x4 (&pk)[NKS]) {
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][i], a.scale_log2, -base));
-        const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][i + 1], a.scale_log2, -base));
-        ls += p0;
-        ls += p1;
+        const float p0 = exp2_fast(__builtin_fmaf(s[kb][i], a.scale_log2, -base));
+        const float p1 = exp2_fast(__builtin_fmaf(s[kb][i + 1], a.scale_log2, -base));
+        ls[(i >> 1) & 3] += p0 + p1;
         pk[kb * 2 + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0, p1);
       }
-    }
-    l += ls;
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  // O^T += V^T . P^T over this wave's keys (key order matches the S^T layout).
+  auto pv = [&](const char* vst, const u32x4 (&pk)[NKS]) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma_pv(*(const u32x4*)(vst + va_off[ks] + db * 32 * (BN * 2)), pk[ks],
+                           oacc[db]);
+  };
+  // Every wave computes every tile of the block, including key halves that
+  // lie wholly above its queries (they come out as P = 0): all waves meet at
+  // each tile's barrier, so skipping them would not shorten the tile, and
+  // uniform control flow keeps the pipelined accumulators in place.
+  if constexpr (PIPE) {
+    // Software pipeline: while the VALU turns S(t) into P(t), the matrix core
+    // computes S(t+1). LDS holds two K tiles and two V^T tiles: iteration t
+    // reads K(t+1) and V(t) while K(t+2) and V(t+1) arrive.
+    constexpr unsigned KST[2] = {0, KT};
+    constexpr unsigned VST[2] = {2 * KT, 2 * KT + VT};
+    f32x16 sa[NKB], sb[NKB];
+    if (ntiles > 0) { issue_k(0, KST[0]); issue_v(0, VST[0]); }
+    if (ntiles > 1) issue_k(1, KST[1]);
+    dma_wait();
+    __syncthreads();
+    if (ntiles > 0) qk(lds + KST[0], sa);
+    __syncthreads();   // K(0) is read everywhere before K(2) overwrites it
 
-    // O^T += V^T . P^T over this tile's keys (key order matches the S^T layout).
+    auto iter = [&](int t, auto parity, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
+      constexpr int P = decltype(parity)::value;
+      if (t + 2 < ntiles) issue_k(t + 2, KST[P]);
+      if (t + 1 < ntiles) issue_v(t + 1, VST[1 - P]);
+      const float base = prep(cur, t * BN + kh * KW);
+      u32x4 pk[NKS];
+      if (t + 1 < ntiles) {
+        qk(lds + KST[1 - P], nxt);
+        expo(cur, base, pk);
+        // interleave the S(t+1) MFMAs with the exponentials of tile t
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const unsigned short* vr =
-            vt_lds + (db * 32 + n) * VSTR + (ks >> 1) * 32 + (ks & 1) * 16 + hh * 4;
-        const u32x2 v0 = *(const u32x2*)(vr);
-        const u32x2 v1 = *(const u32x2*)(vr + 8);
-        const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
-        oacc[db] = mfma_pv(va, pk[ks], oacc[db]);
+        for (int i = 0; i < NKB * NKK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+        }
+      } else {
+        expo(cur, base, pk);
       }
+      pv(lds + VST[P], pk);
+      dma_wait();        // this wave's part of K(t+2), V(t+1) has landed
+      __syncthreads();   // ... everywhere; K(t+1) and V(t) may be overwritten next
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      iter(t, std::integral_constant<int, 0>{}, sa, sb);
+      if (t + 1 < ntiles) iter(t + 1, std::integral_constant<int, 1>{}, sb, sa);
+    }
+  } else {
+    // Plain double buffer: tile t+1 (K and V^T together) arrives while tile t
+    // is computed from the other stage.
+    constexpr unsigned ST_[2] = {0, STAGE};
+    auto step = [&](int t, auto stage) {
+      constexpr int ST = decltype(stage)::value;
+      if (t + 1 < ntiles) { issue_k(t + 1, ST_[1 - ST]); issue_v(t + 1, ST_[1 - ST] + KT); }
+      f32x16 sc[NKB];
+      qk(lds + ST_[ST], sc);
+      const float base = prep(sc, t * BN + kh * KW);
+      u32x4 pk[NKS];
+      expo(sc, base, pk);
+      pv(lds + ST_[ST] + KT, pk);
+      dma_wait();        // this wave's part of tile t+1 has landed
+      __syncthreads();   // tile t+1 landed everywhere; stage ST is free for reuse
+    };
+    if (ntiles > 0) { issue_k(0, ST_[0]); issue_v(0, ST_[0] + KT); }
+    dma_wait();
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, std::integral_constant<int, 0>{});
+      if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
     }
   }
 
-  l += __shfl_xor(l, 32);
-  if (!q_valid) return;
+  float lt;
+  if constexpr (KS == 2) {
+    // Merge the two key halves of every query row. Both waves of a pair publish
+    // (m_used, m_true, l); both compute the common base; wave w+4 writes its O
+    // referred to that base, wave w adds it and finishes the row.
+    xs[((kh * 4 + qw) * 3 + 0) * 64 + lane] = m_used;
+    xs[((kh * 4 + qw) * 3 + 1) * 64 + lane] = m_true;
+    xs[((kh * 4 + qw) * 3 + 2) * 64 + lane] = l;
+    __syncthreads();
+    const int partner = (1 - kh) * 4 + qw;
+    const float mu_o = xs[(partner * 3 + 0) * 64 + lane];
+    const float mt_o = xs[(partner * 3 + 1) * 64 + lane];
+    const float l_o = xs[(partner * 3 + 2) * 64 + lane];
+    const float mc = fmaxf(m_used, mu_o);
+    const float f_me = exp2_fast(m_used - mc);
+    float* xo = (float*)lds;                                   // [4 pairs][NDB*16][64 lanes]
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          xo[((qw * NDB + db) * 16 + i) * 64 + lane] = oacc[db][i] * f_me;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        oacc[db][i] = __builtin_fmaf(oacc[db][i], f_me, xo[((qw * NDB + db) * 16 + i) * 64 + lane]);
+    lt = sum_halves(l * f_me + l_o * exp2_fast(mu_o - mc));
+    m_used = mc;
+    m_true = fmaxf(m_true, mt_o);
+    if (!q_valid) return;
+  } else {
+    lt = sum_halves(l);
+    if (!q_valid) return;
+  }
 
   // Refer the outputs back to the true row max: factor = 2^((m_used - kShift) - m_true).
   const float to_true = exp2_fast(m_used - kShift - m_true);
-  const float row_sum = l * to_true;
   float* orow = a.o + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh;
-  const float f = UNNORM ? to_true : 1.0f / l;
+  const float f = UNNORM ? to_true : 1.0f / lt;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -321,35 +522,52 @@ prefill_kernel(PrefillArgs a) {
   }
   if (hh == 0) {
     const int64_t ri = ((int64_t)b * a.n_heads_q + h) * a.seqlen_q + qi;
-    a.lse[ri] = (m_used - kShift + __log2f(l)) * kLn2;
-    if (a.row_sum) a.row_sum[ri] = row_sum;
+    a.lse[ri] = (m_used - kShift + __log2f(lt)) * kLn2;
+    if (a.row_sum) a.row_sum[ri] = lt * to_true;
   }
 }
 
-template <int D, int BN, bool BF16>
-hipError_t launch_d(const PrefillArgs& a, bool unnorm, hipStream_t stream) {
-  const dim3 grid(a.n_heads_q, (a.seqlen_q + kBM - 1) / kBM, a.batch);
+template <int D, bool BF16>
+hipError_t launch_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hipStream_t stream) {
+  constexpr int BN = tile_keys(D);
+  const int ntiles = (a.seqlen_kv + BN - 1) / BN;
+  const int units = ntiles * (BN / 8) * (D / 8);
+  hipLaunchKernelGGL((vt_pack_kernel<D, BF16>), dim3((units + 255) / 256, a.n_heads_kv, a.batch),
+                     dim3(256), 0, stream, (const unsigned short*)a.v, a.v_sb, a.v_ss, a.v_sh,
+                     a.seqlen_kv, a.n_heads_kv, ntiles, (unsigned short*)w.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int BM = block_rows(D);
+  const dim3 grid(a.n_heads_q, (a.seqlen_q + BM - 1) / BM, a.batch);
   if (unnorm)
-    hipLaunchKernelGGL((prefill_kernel<D, BN, BF16, true>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BF16, true>), grid, dim3(kThreads), 0, stream, a,
+                       (const unsigned short*)w.ws);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BN, BF16, false>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BF16, false>), grid, dim3(kThreads), 0, stream, a,
+                       (const unsigned short*)w.ws);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, bool unnormalized,
-                          hipStream_t stream) {
+size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int head_dim) {
+  const size_t bn = tile_keys(head_dim);
+  const size_t ntiles = ((size_t)seqlen_kv + bn - 1) / bn;
+  return (size_t)batch * n_heads_kv * ntiles * bn * head_dim * 2;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
+                          bool unnormalized, hipStream_t stream) {
   switch (head_dim) {
     case 64:
-      return bf16 ? launch_d<64, 64, true>(a, unnormalized, stream)
-                  : launch_d<64, 64, false>(a, unnormalized, stream);
+      return bf16 ? launch_d<64, true>(a, w, unnormalized, stream)
+                  : launch_d<64, false>(a, w, unnormalized, stream);
     case 128:
-      return bf16 ? launch_d<128, 64, true>(a, unnormalized, stream)
-                  : launch_d<128, 64, false>(a, unnormalized, stream);
+      return bf16 ? launch_d<128, true>(a, w, unnormalized, stream)
+                  : launch_d<128, false>(a, w, unnormalized, stream);
     case 256:
-      return bf16 ? launch_d<256, 32, true>(a, unnormalized, stream)
-                  : launch_d<256, 32, false>(a, unnormalized, stream);
+      return bf16 ? launch_d<256, true>(a, w, unnormalized, stream)
+                  : launch_d<256, false>(a, w, unnormalized, stream);
     default:
       return hipErrorInvalidValue;
   }

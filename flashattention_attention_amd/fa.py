@@ -28,7 +28,9 @@ _i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_v
 _SIGNATURES = {
     "fa_prefill_fwd": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                         _vp, _i64, _i64, _i64, _vp, _vp,
-                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp], _i32),
+                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                        _vp, ctypes.c_uint64, _vp], _i32),
+    "fa_prefill_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
     "fa_decode_plan": ([_i32, _i32, _i64, _i32, _i32, ctypes.POINTER(_i32),
                         ctypes.POINTER(_i32)], _i32),
     "fa_decode_split_partial": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
@@ -114,8 +116,12 @@ def _default_scale(head_dim: int) -> float:
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True,
             softmax_scale: Optional[float] = None, out_unnormalized: bool = False,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            row_sum: Optional[torch.Tensor] = None, want_row_sum: bool = False):
+            row_sum: Optional[torch.Tensor] = None, want_row_sum: bool = False,
+            workspace: Optional[torch.Tensor] = None):
     """Attention forward. q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (fp16/bf16, D contiguous).
+
+    ``workspace`` (optional) is a uint8 GPU tensor of at least
+    ``prefill_workspace_size(...)`` bytes; one is allocated when omitted.
 
     Returns (o, lse) or (o, lse, row_sum) when ``out_unnormalized`` or
     ``want_row_sum``; o is fp32 [B,Sq,Hq,D] (un-normalized when asked), lse and
@@ -151,6 +157,12 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
                               or not t.is_contiguous()):
             raise FAError("lse / row_sum must be contiguous fp32 [B,Hq,Sq]")
     lib = load_library()
+    ws_need = lib.fa_prefill_workspace_size(B, Skv, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    _on_gpu(workspace)
+    if workspace.numel() * workspace.element_size() < ws_need:
+        raise FAError(f"workspace holds {workspace.numel()} bytes, {ws_need} needed")
     st = lib.fa_prefill_fwd(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
@@ -158,9 +170,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
         B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
-        1 if out_unnormalized else 0, _stream(dev))
+        1 if out_unnormalized else 0, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st, "fa_prefill_fwd")
     return (out, lse, row_sum) if need_rs else (out, lse)
+
+
+def prefill_workspace_size(batch: int, seqlen_kv: int, n_heads_kv: int, head_dim: int) -> int:
+    """Bytes of workspace fa_prefill_fwd needs for these sizes."""
+    return int(load_library().fa_prefill_workspace_size(batch, seqlen_kv, n_heads_kv, head_dim))
 
 
 def decode_plan(batch: int, n_heads_kv: int, kv_lens: Sequence[int],

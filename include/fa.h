@@ -78,10 +78,19 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  *   (m_i the row's true max), row_sum = l_i (required); the caller normalizes
  *   o / row_sum.
  *
+ * workspace: caller-owned device scratch of at least
+ * fa_prefill_workspace_size(batch, seqlen_kv, n_heads_kv, head_dim) bytes,
+ * 256-byte aligned. The call first repacks V into it (fp16, transposed per
+ * 64-key tile), then runs the attention kernel; its contents are undefined
+ * afterwards and it must not be shared by calls that overlap in time.
+ *
  * Supported set: head_dim in {64, 128, 256}; dtype FA_F16 or FA_BF16;
  * n_heads_q % n_heads_kv == 0; 1 <= seqlen_q <= seqlen_kv; batch >= 1;
  * softmax_scale finite and > 0; q/k/v/o base pointers 16-byte aligned; q/k/v
- * stride_s, stride_h and stride_b multiples of 8, o strides multiples of 4.
+ * stride_s, stride_h and stride_b multiples of 8, o strides multiples of 4;
+ * k stride_s at most 2^23 elements.
+ * V values of bf16 inputs are taken to fp16 for the P.V contraction (exact in
+ * fp16's normal range; |v| >= 65520 overflows and is outside the contract).
  * The inputs are read, never written; o/lse/row_sum are written in full.
  */
 int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
@@ -91,7 +100,15 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                    float* lse, float* row_sum,
                    int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                    int head_dim, int dtype, int causal, float softmax_scale,
-                   int out_unnormalized, void* stream);
+                   int out_unnormalized, void* workspace, uint64_t workspace_bytes,
+                   void* stream);
+
+/*
+ * fa_prefill_workspace_size — bytes of workspace fa_prefill_fwd needs
+ * (batch * n_heads_kv * ceil(seqlen_kv / 64) * head_dim * 64 * 2). Returns 0
+ * for non-positive sizes. Host only; never fails otherwise.
+ */
+uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int head_dim);
 
 /*
  * fa_decode_plan — deterministic split plan for split-KV decode (host only).

@@ -22,8 +22,9 @@ def _gpu_visible():
 
 def test_exports_every_declared_symbol():
     names = fa.declared_functions()
-    assert set(names) == {"fa_prefill_fwd", "fa_decode_plan", "fa_decode_split_partial",
-                          "fa_decode_merge_lse", "fa_status_string", "fa_last_error"}
+    assert set(names) == {"fa_prefill_fwd", "fa_prefill_workspace_size", "fa_decode_plan",
+                          "fa_decode_split_partial", "fa_decode_merge_lse", "fa_status_string",
+                          "fa_last_error"}
     lib = ctypes.CDLL(fa.library_path())
     for name in names:
         assert hasattr(lib, name), name
@@ -68,14 +69,14 @@ def _prefill(**kw):
     base = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED, row_sum=None,
                 B=1, Sq=128, Skv=128, Hq=4, Hkv=2, D=128, dtype=0, causal=1, scale=0.125,
                 unnorm=0, qs=(128 * 4 * 128, 4 * 128, 128), ks=(128 * 2 * 128, 2 * 128, 128),
-                os=(128 * 4 * 128, 4 * 128, 128))
+                os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40)
     base.update(kw)
     b = base
     lib = fa.load_library()
     return lib.fa_prefill_fwd(b["q"], *b["qs"], b["k"], *b["ks"], b["v"], *b["ks"],
                               b["o"], *b["os"], b["lse"], b["row_sum"], b["B"], b["Sq"],
                               b["Skv"], b["Hq"], b["Hkv"], b["D"], b["dtype"], b["causal"],
-                              b["scale"], b["unnorm"], None)
+                              b["scale"], b["unnorm"], b["ws"], b["wsb"], None)
 
 
 @pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
@@ -87,6 +88,7 @@ def _prefill(**kw):
     (dict(scale=-1.0), 1), (dict(q=ALIGNED + 2), 1), (dict(o=ALIGNED + 4), 1),
     (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1), (dict(os=(128, 2, 128)), 1),
     (dict(ks=(-8, 256, 128)), 1), (dict(Sq=70000 * 128, Skv=70000 * 128), 2),
+    (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(ws=ALIGNED + 16), 1),
 ])
 def test_prefill_validation(kw, status):
     st = _prefill(**kw)
@@ -124,6 +126,14 @@ def test_decode_merge_validation(kw, status):
     st = lib.fa_decode_merge_lse(b["po"], b["pl"], b["lens"], b["B"], b["Hq"], b["D"],
                                  b["split"], b["ms"], b["o"], b["lse"], None)
     assert st == status
+
+
+def test_workspace_size():
+    lib = fa.load_library()
+    assert lib.fa_prefill_workspace_size(1, 3314, 4, 128) == 1 * 4 * 52 * 64 * 128 * 2
+    assert lib.fa_prefill_workspace_size(2, 64, 1, 64) == 2 * 1 * 1 * 64 * 64 * 2
+    assert lib.fa_prefill_workspace_size(1, 100, 2, 256) == 1 * 2 * 2 * 64 * 256 * 2
+    assert lib.fa_prefill_workspace_size(0, 64, 1, 64) == 0
 
 
 def test_binding_rejects_cpu_tensors():
