@@ -67,7 +67,7 @@ def decode_setup(torch, fa, cfg, split_len=None):
     offs = torch.from_numpy(x["kv_offsets"]).cuda()
     lens = torch.from_numpy(x["kv_lens"]).cuda()
     if split_len is None:
-        split_len, max_splits = fa.decode_plan(cfg.batch, cfg.n_heads_kv, x["kv_lens"])
+        split_len, max_splits = fa.decode_plan(x["kv_lens"], cfg.n_heads_q, cfg.n_heads_kv, cfg.head_dim)
     else:
         max_splits = -(-int(x["kv_lens"].max()) // split_len)
     B, Hq, D = x["q"].shape
@@ -292,6 +292,14 @@ def main():
         print("[bench] long decode", file=sys.stderr, flush=True)
 
         lcfg = inputs.LONG_DECODE
+        if args.split_sweep:
+            sweep = {}
+            for sl in (512, 1024, 1536, 2048, 3072, 4096):
+                p2, m2, i2 = decode_setup(torch, fa, lcfg, split_len=sl)
+                c = time_calls(torch, [p2, m2], 5, flush=flush)
+                sweep[sl] = round((c[0]["median_ms"] + c[1]["median_ms"]) * 1e3, 1)
+                del p2, m2
+            line["decode_batched_long_us_by_split_len"] = sweep
         l_partial, l_merge, linfo = decode_setup(torch, fa, lcfg)
         for _ in range(3):
             l_partial(); l_merge()

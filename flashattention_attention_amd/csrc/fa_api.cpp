@@ -124,23 +124,61 @@ uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int
   return fa::prefill_workspace_bytes(batch, seqlen_kv, n_heads_kv, head_dim);
 }
 
-int fa_decode_plan(int batch, int n_heads_kv, int64_t total_kv_len, int max_kv_len,
-                   int num_cus, int* split_len_out, int* max_splits_out) {
-  if (!split_len_out || !max_splits_out)
-    return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: null output pointer");
-  if (batch < 1 || n_heads_kv < 1 || max_kv_len < 1 || num_cus < 1 ||
-      total_kv_len < max_kv_len || total_kv_len > (int64_t)batch * max_kv_len)
-    return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: inconsistent sizes");
-  // Aim for about 8 work items (one wave each) per compute unit, in splits
-  // of at least 32 keys and a multiple of 32, so that short caches still
-  // spread over many waves and long caches keep partial traffic small.
-  const int64_t target_items = (int64_t)num_cus * 8;
-  int64_t per = (total_kv_len * n_heads_kv + target_items - 1) / target_items;
-  int64_t split = ((per + 31) / 32) * 32;
-  if (split < 32) split = 32;
-  if (split > max_kv_len) split = ((int64_t)max_kv_len + 15) / 16 * 16;
-  *split_len_out = (int)split;
-  *max_splits_out = (int)(((int64_t)max_kv_len + split - 1) / split);
+int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_heads_kv,
+                   int head_dim, int num_cus, int* split_len_out, int* max_splits_out) {
+  if (!kv_lens_host || !split_len_out || !max_splits_out)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: null pointer argument");
+  if (batch < 1 || n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0 ||
+      num_cus < 1)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: bad batch, head counts or num_cus");
+  if (!head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_plan: head_dim %d not in {64, 128, 256}",
+                head_dim);
+  int max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (kv_lens_host[b] < 1)
+      return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: kv_lens[%d] = %d < 1", b, kv_lens_host[b]);
+    if (kv_lens_host[b] > max_len) max_len = kv_lens_host[b];
+  }
+  const int g = fa::decode_heads_per_wave(n_heads_q / n_heads_kv);
+  const int bk = fa::decode_block_rows(head_dim, g);
+  const int64_t slots = (int64_t)num_cus * fa::decode_waves_per_cu(head_dim);
+  const int64_t groups = n_heads_q / g;    // waves per (sequence, split)
+  auto waves_of = [&](int64_t sl, int64_t* max_ns) {
+    int64_t w = 0, mx = 0;
+    for (int b = 0; b < batch; ++b) {
+      const int64_t ns = (kv_lens_host[b] + sl - 1) / sl;
+      w += ns;
+      if (ns > mx) mx = ns;
+    }
+    if (max_ns) *max_ns = mx;
+    return w * groups;
+  };
+  // Candidates are whole blocks of rows. Two regimes:
+  //  * everything fits in one round of resident waves even at one block per
+  //    split: latency-bound; minimize the rows a wave streams plus ~0.6 row
+  //    per split the merge reads;
+  //  * otherwise bandwidth-bound: maximize how full the rounds of resident
+  //    waves are (a half-empty last round costs nearly a full one), with a
+  //    small charge per extra round; ties go to the shorter split.
+  int best = bk;
+  double best_score = -1e300;
+  const bool latency_bound = waves_of(bk, nullptr) <= slots;
+  for (int64_t sl = bk;; sl += bk) {
+    int64_t max_ns = 0;
+    const int64_t waves = waves_of(sl, &max_ns);
+    const int64_t rounds = (waves + slots - 1) / slots;
+    const double score = latency_bound
+                             ? -((double)sl + 0.6 * (double)max_ns)
+                             : (double)waves / (double)(rounds * slots) - 0.04 * (double)rounds;
+    if (score > best_score) {
+      best_score = score;
+      best = (int)sl;
+    }
+    if (sl >= max_len) break;
+  }
+  *split_len_out = best;
+  *max_splits_out = (max_len + best - 1) / best;
   return ok();
 }
 

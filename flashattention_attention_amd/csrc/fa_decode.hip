@@ -88,12 +88,14 @@ decode_partial_kernel(DecodeArgs a) {
   constexpr int EPL = D / LPK;             // elements per lane: 8 or 16
   constexpr int W = EPL / 8;               // 16-byte loads per row per lane
   constexpr int KPS = 64 / LPK;            // rows per load step: 4 or 8
-  constexpr int NB = D == 256 ? 2 : 4;     // load steps per block
+  // load steps per block: 16 KB of K+V per block, halved when the wave serves
+  // more than 4 heads (their accumulators need the registers)
+  constexpr int NB = D == 256 ? (G > 4 ? 2 : 4) : (G > 4 ? 4 : 8);
   constexpr int BK = KPS * NB;             // rows per block
 
   const int lane = threadIdx.x;
-  const int s = blockIdx.x;
-  const int h0 = blockIdx.y * G;
+  const int h0 = blockIdx.x * G;   // head groups fastest: the waves reading the
+  const int s = blockIdx.y;        // same tokens' rows are dispatched together
   const int b = blockIdx.z;
   const int hk = h0 / (a.n_heads_q / a.n_heads_kv);
   const int L = a.kv_lens[b];
@@ -118,18 +120,16 @@ decode_partial_kernel(DecodeArgs a) {
   const unsigned short* vbase =
       (const unsigned short*)a.v + row0 * a.kv_st + (int64_t)hk * a.kv_sh + c * EPL;
 
-  u32x4 kr[NB][W], vr[NB][W];
+  // Load one block of rows. Rows past hi repeat row hi-1 (always valid
+  // memory); their scores are masked to -inf, so they contribute exactly 0.
   auto load_block = [&](int start, u32x4 (&kd)[NB][W], u32x4 (&vd)[NB][W]) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int key = start + j * KPS + slot;
-      const bool ok = key < hi;
+      const int64_t key = min(start + j * KPS + slot, hi - 1);
 #pragma unroll
       for (int w = 0; w < W; ++w) {
-        kd[j][w] = ok ? *(const u32x4*)(kbase + (int64_t)key * a.kv_st + w * 8)
-                      : u32x4{0, 0, 0, 0};
-        vd[j][w] = ok ? *(const u32x4*)(vbase + (int64_t)key * a.kv_st + w * 8)
-                      : u32x4{0, 0, 0, 0};
+        kd[j][w] = __builtin_nontemporal_load((const u32x4*)(kbase + key * a.kv_st + w * 8));
+        vd[j][w] = __builtin_nontemporal_load((const u32x4*)(vbase + key * a.kv_st + w * 8));
       }
     }
   };
@@ -143,11 +143,7 @@ decode_partial_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
   }
 
-  load_block(lo, kr, vr);
-  for (int start = lo; start < hi; start += BK) {
-    u32x4 kn[NB][W], vn[NB][W];
-    if (start + BK < hi) load_block(start + BK, kn, vn);
-
+  auto compute_block = [&](int start, const u32x4 (&kr)[NB][W], const u32x4 (&vr)[NB][W]) {
     // Scores (log2 units) of this lane's rows, one per step and head.
     float sc[NB][G];
 #pragma unroll
@@ -164,7 +160,6 @@ decode_partial_kernel(DecodeArgs a) {
         sc[j][g] = ok ? d * a.scale_log2 : -INFINITY;
       }
     }
-
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       // Block max over the NB*KPS rows: in-lane over the steps, then across the
@@ -198,16 +193,18 @@ decode_partial_kernel(DecodeArgs a) {
           }
       }
     }
+  };
 
-    if (start + BK < hi) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          kr[j][w] = kn[j][w];
-          vr[j][w] = vn[j][w];
-        }
-    }
+  // Two register buffers in turn: while one block is computed the next one is
+  // in flight (the loop is unrolled by two so no buffer is ever copied).
+  u32x4 ka[NB][W], va[NB][W], kb[NB][W], vb[NB][W];
+  load_block(lo, ka, va);
+  for (int start = lo; start < hi; start += 2 * BK) {
+    if (start + BK < hi) load_block(start + BK, kb, vb);
+    compute_block(start, ka, va);
+    if (start + BK >= hi) break;
+    if (start + 2 * BK < hi) load_block(start + 2 * BK, ka, va);
+    compute_block(start + BK, kb, vb);
   }
 
   // Sum the row slots (m is the same in every lane), then write the partial.
@@ -235,10 +232,14 @@ decode_partial_kernel(DecodeArgs a) {
   }
 }
 
+// One wave per (sequence, query head). Split LSEs are read lane-parallel and
+// reduced across the wave; the weighted sum of the split outputs runs over
+// the splits in index order with the loads of several splits in flight.
 template <int D>
 __global__ void __launch_bounds__(64)
 decode_merge_kernel(MergeArgs a) {
   constexpr int EPL = D / 64;
+  constexpr int U = 32;                    // splits in flight per step
   const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -248,33 +249,55 @@ decode_merge_kernel(MergeArgs a) {
   const int ns = L < 1 ? 0 : (L + a.split_len - 1) / a.split_len;
   if (ns < 1 || ns > a.max_splits) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) out[lane + 64 * e] = __builtin_nanf("");
+    for (int e = 0; e < EPL; ++e) out[lane * EPL + e] = __builtin_nanf("");
     if (lane == 0) a.lse[bh] = __builtin_nanf("");
     return;
   }
   const float* pl = a.part_lse + bh * a.max_splits;
-  const float* po = a.part_o + bh * a.max_splits * D;
+  const float* po = a.part_o + bh * a.max_splits * D + lane * EPL;
+
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pl[s]);
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) M = fmaxf(M, pl[s0 + lane]);
+#pragma unroll
+  for (int x = 1; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
+
   float wsum = 0.0f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __expf(pl[s] - M);
-    wsum += w;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const float wl = s0 + lane < ns ? __expf(pl[s0 + lane] - M) : 0.0f;
+    wsum += wl;
+    const int n = min(64, ns - s0);
+    for (int j = 0; j < n; j += U) {
+      float v[U][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(w, po[(int64_t)s * D + lane + 64 * e],
-                                                          acc[e]);
+      for (int u = 0; u < U; ++u) {
+        const int sj = s0 + min(j + u, n - 1);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[u][e] = po[(int64_t)sj * D + e];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (j + u < n) {
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u));
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(w, v[u][e], acc[e]);
+        }
+      }
+    }
   }
+#pragma unroll
+  for (int x = 1; x < 64; x *= 2) wsum += __shfl_xor(wsum, x);
   const float inv = 1.0f / wsum;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) out[lane + 64 * e] = acc[e] * inv;
+  for (int e = 0; e < EPL; ++e) out[lane * EPL + e] = acc[e] * inv;
   if (lane == 0) a.lse[bh] = M + __logf(wsum);
 }
 
 template <int D, bool BF16>
 hipError_t launch_partial_d(const DecodeArgs& a, int g, hipStream_t stream) {
-  const dim3 grid(a.max_splits, a.n_heads_q / g, a.batch);
+  const dim3 grid(a.n_heads_q / g, a.max_splits, a.batch);
   switch (g) {
 #define FA_CASE(G) \
   case G: hipLaunchKernelGGL((decode_partial_kernel<D, G, BF16>), grid, dim3(64), 0, stream, a); break;
@@ -289,15 +312,24 @@ hipError_t launch_partial_d(const DecodeArgs& a, int g, hipStream_t stream) {
 }  // namespace
 
 // Heads served per wave: the largest divisor of the GQA group that is <= 8.
-static int heads_per_wave(int group) {
+int decode_heads_per_wave(int group) {
   for (int g = 8; g >= 1; --g)
     if (group % g == 0) return g;
   return 1;
 }
 
+// Rows per block of the partial kernel and resident waves per compute unit
+// (from its register use: 2 waves per SIMD below head_dim 256, else 1).
+int decode_block_rows(int head_dim, int g) {
+  const int kps = head_dim >= 128 ? 4 : 8;
+  const int nb = head_dim == 256 ? (g > 4 ? 2 : 4) : (g > 4 ? 4 : 8);
+  return kps * nb;
+}
+int decode_waves_per_cu(int head_dim) { return head_dim == 256 ? 4 : 8; }
+
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                                  hipStream_t stream) {
-  const int g = heads_per_wave(a.n_heads_q / a.n_heads_kv);
+  const int g = decode_heads_per_wave(a.n_heads_q / a.n_heads_kv);
   switch (head_dim) {
     case 64: return bf16 ? launch_partial_d<64, true>(a, g, stream)
                          : launch_partial_d<64, false>(a, g, stream);

@@ -63,4 +63,9 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                                  hipStream_t stream);
 hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 
+// Geometry of the decode partial kernel, for the split planner.
+int decode_heads_per_wave(int group);
+int decode_block_rows(int head_dim, int heads_per_wave);
+int decode_waves_per_cu(int head_dim);
+
 }  // namespace fa

@@ -31,8 +31,8 @@ _SIGNATURES = {
                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, ctypes.c_uint64, _vp], _i32),
     "fa_prefill_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
-    "fa_decode_plan": ([_i32, _i32, _i64, _i32, _i32, ctypes.POINTER(_i32),
-                        ctypes.POINTER(_i32)], _i32),
+    "fa_decode_plan": ([ctypes.POINTER(ctypes.c_int32), _i32, _i32, _i32, _i32, _i32,
+                        ctypes.POINTER(_i32), ctypes.POINTER(_i32)], _i32),
     "fa_decode_split_partial": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp],
                                 _i32),
@@ -181,16 +181,17 @@ def prefill_workspace_size(batch: int, seqlen_kv: int, n_heads_kv: int, head_dim
     return int(load_library().fa_prefill_workspace_size(batch, seqlen_kv, n_heads_kv, head_dim))
 
 
-def decode_plan(batch: int, n_heads_kv: int, kv_lens: Sequence[int],
+def decode_plan(kv_lens: Sequence[int], n_heads_q: int, n_heads_kv: int, head_dim: int,
                 num_cus: Optional[int] = None) -> Tuple[int, int]:
     """Deterministic (split_len, max_splits) for host-known KV lengths."""
     lens = [int(x) for x in kv_lens]
     if num_cus is None:
         num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    arr = (ctypes.c_int32 * len(lens))(*lens)
     lib = load_library()
     sl, ms = _i32(), _i32()
-    st = lib.fa_decode_plan(batch, n_heads_kv, sum(lens), max(lens), num_cus, ctypes.byref(sl),
-                            ctypes.byref(ms))
+    st = lib.fa_decode_plan(arr, len(lens), n_heads_q, n_heads_kv, head_dim, num_cus,
+                            ctypes.byref(sl), ctypes.byref(ms))
     _check(st, "fa_decode_plan")
     return sl.value, ms.value
 

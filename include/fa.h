@@ -118,14 +118,18 @@ uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int
  * ranges; the split count is part of the float summation order, so it must
  * be a fixed function of the shape).
  *
- * Chooses split_len (keys per split, a multiple of 16) so that the
- * (sequence, KV head, split) work items cover num_cus compute units several
- * times over, and max_splits = ceil(max_kv_len / split_len). The result is a
- * pure function of the arguments. Pass total_kv_len = sum of all sequence
- * lengths. Returns FA_ERR_INVALID_ARG for non-positive sizes or null outputs.
+ * kv_lens_host: HOST array [batch] of sequence lengths (each >= 1). Chooses
+ * split_len (keys per split, a whole number of the partial kernel's row
+ * blocks, so a multiple of 16) to minimize a cost model of the partial and
+ * merge kernels: the work items (sequence, group of query heads, split) run
+ * in rounds of num_cus * (resident waves per CU), and each round lasts as long
+ * as its longest split. max_splits_out = ceil(max(kv_lens) / split_len). The
+ * result is a pure function of the arguments. Returns FA_ERR_INVALID_ARG for
+ * null pointers, lengths < 1 or bad head counts, FA_ERR_UNSUPPORTED for an
+ * unsupported head_dim.
  */
-int fa_decode_plan(int batch, int n_heads_kv, int64_t total_kv_len, int max_kv_len,
-                   int num_cus, int* split_len_out, int* max_splits_out);
+int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_heads_kv,
+                   int head_dim, int num_cus, int* split_len_out, int* max_splits_out);
 
 /*
  * fa_decode_split_partial — per-split partial attention for one query token.

@@ -38,31 +38,44 @@ def test_status_strings():
     assert lib.fa_status_string(3) == b"FA_ERR_HIP"
 
 
-def _plan(b, hkv, total, mx, cus=256):
+def _plan(lens, hq, hkv, d=128, cus=256):
     lib = fa.load_library()
     sl, ms = ctypes.c_int(), ctypes.c_int()
-    st = lib.fa_decode_plan(b, hkv, total, mx, cus, ctypes.byref(sl), ctypes.byref(ms))
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    st = lib.fa_decode_plan(arr if lens is not None else None, len(lens), hq, hkv, d, cus,
+                            ctypes.byref(sl), ctypes.byref(ms))
     return st, sl.value, ms.value
 
 
-def test_decode_plan_is_pure_and_covers_lengths():
-    for b, hkv, lens in [(1, 4, [1641]), (32, 8, [512 + 997 * i for i in range(32)]),
-                         (3, 2, [1, 29, 52]), (1, 1, [1])]:
-        st, sl, ms = _plan(b, hkv, sum(lens), max(lens))
-        assert st == 0
-        assert sl % 16 == 0 and sl >= 16
-        assert ms == -(-max(lens) // sl)
-        assert (st, sl, ms) == _plan(b, hkv, sum(lens), max(lens))
+@pytest.mark.parametrize("lens,hq,hkv,d", [([1641], 28, 4, 128),
+                                           ([512 + 997 * i for i in range(32)], 32, 8, 128),
+                                           ([1, 29, 52], 4, 2, 64), ([1], 1, 1, 256),
+                                           ([100000] * 3, 16, 2, 128)])
+def test_decode_plan_is_pure_and_covers_lengths(lens, hq, hkv, d):
+    st, sl, ms = _plan(lens, hq, hkv, d)
+    assert st == 0
+    assert sl % 16 == 0 and sl >= 16
+    assert ms == -(-max(lens) // sl)
+    assert (st, sl, ms) == _plan(lens, hq, hkv, d)
+
+
+def test_decode_plan_prefers_one_round():
+    # 32 long sequences x 8 KV heads: the chosen split keeps the wave count
+    # within one round of resident waves (256 CUs x 8).
+    lens = [int(x) for x in __import__("numpy").random.default_rng(4).integers(512, 32769, 32)]
+    st, sl, ms = _plan(lens, 32, 8, 128)
+    waves = sum(-(-L // sl) for L in lens) * 8
+    assert st == 0 and waves <= 2048
 
 
 @pytest.mark.parametrize("args", [
-    (0, 4, 10, 10, 256), (1, 0, 10, 10, 256), (1, 4, 10, 0, 256), (1, 4, 10, 10, 0),
-    (2, 4, 5, 10, 256),      # total < max
-    (2, 4, 25, 10, 256),     # total > batch * max
+    dict(lens=[0]), dict(lens=[5, -1]), dict(hq=0), dict(hkv=3), dict(cus=0), dict(d=96),
 ])
 def test_decode_plan_rejects(args):
-    st, _, _ = _plan(*args)
-    assert st == fa.FA_ERR_INVALID_ARG
+    kw = dict(lens=[10], hq=4, hkv=2, d=128, cus=256)
+    kw.update(args)
+    st, _, _ = _plan(kw["lens"], kw["hq"], kw["hkv"], kw["d"], kw["cus"])
+    assert st in (fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED)
 
 
 def _prefill(**kw):

@@ -202,7 +202,7 @@ def test_gqa_decode_workload(torch_gpu, split_len):
     _say(cfg.name, split_len)
     x = inputs.make_decode_inputs(cfg)
     if split_len == "plan":
-        split_len, max_splits = fa.decode_plan(cfg.batch, cfg.n_heads_kv, x["kv_lens"])
+        split_len, max_splits = fa.decode_plan(x["kv_lens"], cfg.n_heads_q, cfg.n_heads_kv, cfg.head_dim)
     else:
         max_splits = -(-int(x["kv_lens"].max()) // split_len)
     po, pl, o, lse = _run_decode(torch_gpu, x, cfg.dtype, split_len, max_splits, cfg.scale)
@@ -261,7 +261,7 @@ def test_long_decode_full_size(torch_gpu):
     cfg = inputs.LONG_DECODE
     _say(cfg.name)
     x = inputs.make_decode_inputs(cfg)
-    split_len, max_splits = fa.decode_plan(cfg.batch, cfg.n_heads_kv, x["kv_lens"])
+    split_len, max_splits = fa.decode_plan(x["kv_lens"], cfg.n_heads_q, cfg.n_heads_kv, cfg.head_dim)
     q, kc, vc, offs, lens = _dev_decode(torch, x, cfg.dtype)
     outs = []
     for _ in range(2):
