@@ -10,12 +10,13 @@
 //     work-group that reads the tile (exact for magnitudes in fp16's normal
 //     range).
 //
-//  2. prefill_kernel: one work-group = 8 waves filling one compute unit (2
-//     waves per SIMD) on one (batch, query head). At head_dim <= 128 each
-//     wave owns 32 query rows (256 per work-group) and takes whole 64-key
-//     tiles; at head_dim 256 waves w and w+4 own the same 32 rows (128 per
-//     work-group), each takes half of every tile with its own online softmax,
-//     and the pair is merged at the end.
+//  2. prefill_kernel: one work-group per (query block, query head, batch);
+//     2 waves per SIMD. At head_dim <= 128 a work-group has 4 waves, each
+//     owning 32 query rows (128 per block) and taking whole 64-key tiles, and
+//     two work-groups share a compute unit. At head_dim 256 a work-group has
+//     8 waves: waves w and w+4 own the same 32 rows (128 per block), each
+//     takes half of every tile with its own online softmax, and the pair is
+//     merged at the end.
 //
 // Mapping to the CDNA4 matrix cores (v_mfma_f32_32x32x16_{bf16,f16}): each
 // wave computes the TRANSPOSED score tile S^T = K . Q^T (keys along M, its 32
@@ -69,23 +70,24 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kShift = 7.0f;            // log2 of the fp16 headroom factor on P
 constexpr float kSlack = 8.0f;            // stale-max tolerance (log2 units)
 constexpr float kLn2 = 0.693147180559945309f;
 
-// Work-group geometry per head dim. key_split(d) = 1: eight groups of 32
-// query rows, each wave takes whole 64-key tiles (256 query rows per
-// work-group, so each K/V tile fetched serves 256 rows). key_split(d) = 2
-// (head_dim 256, where a wave cannot hold 64 keys of scores next to its Q and
-// O registers): waves w and w+4 own the same 32 query rows and each takes
-// half of every tile (128 query rows per work-group).
+// Work-group geometry per head dim. key_split(d) = 1: every wave owns its own
+// 32 query rows and takes whole 64-key tiles. key_split(d) = 2 (head_dim 256,
+// where a wave cannot hold 64 keys of scores next to its Q and O registers):
+// waves w and w+4 own the same 32 query rows and each takes half of every
+// tile.
 __host__ __device__ constexpr int key_split(int d) { return d <= 128 ? 1 : 2; }
+// Waves per work-group: 4 at head_dim <= 128 (128 query rows; two work-groups
+// share a compute unit, so one's prologue and epilogue overlap the other's
+// tiles), 8 at head_dim 256 (four wave pairs).
+__host__ __device__ constexpr int wg_waves(int d) { return d <= 128 ? 4 : 8; }
 __host__ __device__ constexpr int tile_keys(int d) {
   return key_split(d) == 1 ? 64 : (d <= 128 ? 128 : 64);
 }
-__host__ __device__ constexpr int block_rows(int d) { return 32 * (8 / key_split(d)); }
+__host__ __device__ constexpr int block_rows(int d) { return 32 * (wg_waves(d) / key_split(d)); }
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
@@ -201,8 +203,9 @@ vt_pack_kernel(const unsigned short* __restrict__ v, int64_t v_sb, int64_t v_ss,
 // Attention forward.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16, bool UNNORM>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(64 * wg_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
+  constexpr int kWaves = wg_waves(D);
   constexpr bool PIPE = D <= 128;            // software-pipelined loop (register budget)
   constexpr int KS = key_split(D);           // waves sharing one query group
   constexpr int QG = kWaves / KS;            // query groups of 32 rows
@@ -224,8 +227,14 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   constexpr int V_INSTR = VT / 1024 / kWaves;
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile too small for the DMA split");
   static_assert(KS == 1 || 4 * NDB * 16 * 64 * 4 <= 2 * STAGE, "LDS too small for the pair merge");
+  static_assert(KS == 1 || NDB * 16 * 64 * 4 == 32 * D * 4, "merge slice must hold 32 O rows");
 
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];   // K/V^T tiles, 2 of each
+  // K/V^T tiles (two of each); after the loop, the per-wave O staging area
+  // (32 rows x D fp32 per wave; at key_split 2 a pair leader reuses its own
+  // merge slice, which has exactly that size).
+  constexpr int OSTG = 32 * D * 4;
+  constexpr int LDS_BYTES = (KS == 1 && kWaves * OSTG > 2 * STAGE) ? kWaves * OSTG : 2 * STAGE;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   __shared__ float xs[KS == 2 ? 2 * 4 * 3 * 64 : 1];   // per-row softmax state, for the pair merge
 
   const int tid = threadIdx.x;
@@ -246,20 +255,21 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   const bool q_valid = qi < a.seqlen_q;
   const int qpos = qi + off;
 
-  // Q^T operand: 8 consecutive dims of this lane's query per k-step.
+  // Q^T operand: 8 consecutive dims of this lane's query per k-step. Loaded
+  // after the first tile's DMA is issued so the two latencies overlap; the
+  // registers are consumed right away so the compiler waits for them here and
+  // not at their first use inside the tile loop (where that wait would also
+  // stall on the prefetch DMA of the next tile).
   u32x4 qr[NKK];
-  {
+  auto load_q = [&]() {
     const unsigned short* qp = (const unsigned short*)a.q + (int64_t)b * a.q_sb +
                                (int64_t)qi * a.q_ss + (int64_t)h * a.q_sh;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qr[kk] = q_valid ? *(const u32x4*)(qp + kk * 16 + hh * 8) : u32x4{0, 0, 0, 0};
-    // Consume the Q registers here so the compiler waits for these loads now,
-    // and not at their first use inside the tile loop (where that wait would
-    // also stall on the prefetch DMA of the next tile).
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qr[kk]));
-  }
+  };
 
   // KV range: keys up to the largest query position of the block.
   int kv_end = a.seqlen_kv;
@@ -410,6 +420,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     f32x16 sa[NKB], sb[NKB];
     if (ntiles > 0) { issue_k(0, KST[0]); issue_v(0, VST[0]); }
     if (ntiles > 1) issue_k(1, KST[1]);
+    load_q();
     dma_wait();
     __syncthreads();
     if (ntiles > 0) qk(lds + KST[0], sa);
@@ -459,6 +470,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
       __syncthreads();   // tile t+1 landed everywhere; stage ST is free for reuse
     };
     if (ntiles > 0) { issue_k(0, ST_[0]); issue_v(0, ST_[0] + KT); }
+    load_q();
     dma_wait();
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
@@ -501,29 +513,43 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     lt = sum_halves(l * f_me + l_o * exp2_fast(mu_o - mc));
     m_used = mc;
     m_true = fmaxf(m_true, mt_o);
-    if (!q_valid) return;
   } else {
     lt = sum_halves(l);
-    if (!q_valid) return;
   }
 
   // Refer the outputs back to the true row max: factor = 2^((m_used - kShift) - m_true).
   const float to_true = exp2_fast(m_used - kShift - m_true);
-  float* orow = a.o + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh;
   const float f = UNNORM ? to_true : 1.0f / lt;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 val = {oacc[db][4 * g] * f, oacc[db][4 * g + 1] * f, oacc[db][4 * g + 2] * f,
-                         oacc[db][4 * g + 3] * f};
-      *(f32x4*)(orow + db * 32 + g * 8 + hh * 4) = val;
-    }
-  }
-  if (hh == 0) {
+  if (hh == 0 && q_valid) {
     const int64_t ri = ((int64_t)b * a.n_heads_q + h) * a.seqlen_q + qi;
     a.lse[ri] = (m_used - kShift + __log2f(lt)) * kLn2;
     if (a.row_sum) a.row_sum[ri] = lt * to_true;
+  }
+
+  // Stage this wave's 32 output rows in LDS ([row][D] fp32, 16-byte chunks
+  // XOR-swizzled by row), then store whole rows: one store instruction then
+  // writes 64 x 16 contiguous bytes instead of 16-byte pieces of 32 rows.
+  constexpr int CPRO = D / 4;                              // 16-byte chunks per O row
+  constexpr int OSW = CPRO < 32 ? CPRO - 1 : 31;
+  float* stg = (float*)(lds + (KS == 1 ? wave : qw) * OSTG);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = (db * 32 + g * 8 + hh * 4) / 4;
+      *(f32x4*)(stg + n * D + ((chunk ^ (n & OSW)) << 2)) =
+          f32x4{oacc[db][4 * g] * f, oacc[db][4 * g + 1] * f, oacc[db][4 * g + 2] * f,
+                oacc[db][4 * g + 3] * f};
+    }
+  const int row_base = q0 + qw * 32;
+  float* obase = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+#pragma unroll
+  for (int it = 0; it < 32 * CPRO / 64; ++it) {
+    const int idx = it * 64 + lane;
+    const int r = idx / CPRO, c = idx % CPRO;
+    const f32x4 val = *(const f32x4*)(stg + r * D + ((c ^ (r & OSW)) << 2));
+    if (row_base + r < a.seqlen_q)
+      *(f32x4*)(obase + (int64_t)(row_base + r) * a.o_ss + c * 4) = val;
   }
 }
 
@@ -540,10 +566,11 @@ hipError_t launch_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hipStrea
   constexpr int BM = block_rows(D);
   const dim3 grid(a.n_heads_q, (a.seqlen_q + BM - 1) / BM, a.batch);
   if (unnorm)
-    hipLaunchKernelGGL((prefill_kernel<D, BF16, true>), grid, dim3(kThreads), 0, stream, a,
+    hipLaunchKernelGGL((prefill_kernel<D, BF16, true>), grid, dim3(64 * wg_waves(D)), 0, stream, a,
                        (const unsigned short*)w.ws);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BF16, false>), grid, dim3(kThreads), 0, stream, a,
+    hipLaunchKernelGGL((prefill_kernel<D, BF16, false>), grid, dim3(64 * wg_waves(D)), 0, stream,
+                       a,
                        (const unsigned short*)w.ws);
   return hipGetLastError();
 }
