@@ -435,17 +435,30 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
       if (t + 1 < ntiles) {
         qk(lds + KST[1 - P], nxt);
         expo(cur, base, pk);
-        // interleave the S(t+1) MFMAs with the exponentials of tile t
+        // Interleave the S(t+1) MFMAs with the exponentials of tile t, with
+        // each MFMA's LDS operand read issued three MFMAs ahead of it.
+        constexpr int NQ = NKB * NKK, AHEAD = 3;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);   // LDS reads
 #pragma unroll
-        for (int i = 0; i < NKB * NKK; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+        for (int i = 0; i < NQ; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+          if (i + AHEAD < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);     // six VALU
         }
       } else {
         expo(cur, base, pk);
       }
       pv(lds + VST[P], pk);
+      {
+        // P.V: V^T operand reads four MFMAs ahead.
+        constexpr int NP = NKS * NDB, AHEAD = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 1);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          if (i + AHEAD < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        }
+      }
       dma_wait();        // this wave's part of K(t+2), V(t+1) has landed
       __syncthreads();   // ... everywhere; K(t+1) and V(t) may be overwritten next
     };
