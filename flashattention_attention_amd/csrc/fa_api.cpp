@@ -91,7 +91,7 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
   if (o_sb < 0 || o_ss < 0 || o_sh < 0 || o_sb % 4 || o_ss % 4 || o_sh % 4)
     return fail(FA_ERR_INVALID_ARG,
                 "fa_prefill_fwd: o strides must be non-negative multiples of 4 elements");
-  if ((seqlen_q + 127) / 128 > 65535 || batch > 65535 || n_heads_q > 65535)
+  if ((int64_t)batch * n_heads_q * ((seqlen_q + 127) / 128) > (1 << 30))
     return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: grid too large (seqlen_q or batch)");
   if (k_ss > (int64_t)(1 << 23))
     return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: k sequence stride above 2^23 elements");

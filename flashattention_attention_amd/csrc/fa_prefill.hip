@@ -80,14 +80,17 @@ constexpr float kLn2 = 0.693147180559945309f;
 // waves w and w+4 own the same 32 query rows and each takes half of every
 // tile.
 __host__ __device__ constexpr int key_split(int d) { return d <= 128 ? 1 : 2; }
-// Waves per work-group: 4 at head_dim <= 128 (128 query rows; two work-groups
-// share a compute unit, so one's prologue and epilogue overlap the other's
-// tiles), 8 at head_dim 256 (four wave pairs).
-__host__ __device__ constexpr int wg_waves(int d) { return d <= 128 ? 4 : 8; }
+// Query heads per work-group (hp): at head_dim <= 128, when the query heads
+// that share a KV head come in pairs, a work-group serves the same 128 query
+// rows of two of them, so every K and V^T tile brought into LDS feeds eight
+// waves while the causal extent of a work-group stays that of 128 rows.
+// Waves per work-group: 4 per query head at head_dim <= 128 (32 rows each),
+// 8 at head_dim 256 (four wave pairs).
+__host__ __device__ constexpr int wg_waves(int d, int hp) { return d <= 128 ? 4 * hp : 8; }
 __host__ __device__ constexpr int tile_keys(int d) {
   return key_split(d) == 1 ? 64 : (d <= 128 ? 128 : 64);
 }
-__host__ __device__ constexpr int block_rows(int d) { return 32 * (wg_waves(d) / key_split(d)); }
+__host__ __device__ constexpr int block_rows(int d) { return 128; }
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
@@ -200,15 +203,75 @@ vt_pack_kernel(const unsigned short* __restrict__ v, int64_t v_sb, int64_t v_ss,
 }
 
 // ---------------------------------------------------------------------------
+// Work-group order. The dispatcher hands work-group i of a launch to XCD
+// i % 8, and each XCD has its own L2. Work-groups are numbered so that (1)
+// the query heads that read one KV head (one "group": a batch entry and a KV
+// head) stay on as few XCDs as possible, so that group's K/V^T tiles are
+// fetched into as few L2s as possible, and (2) on every XCD the longest
+// causal blocks start first. With G groups: G a multiple of 8 gives each XCD
+// G/8 whole groups; G dividing 8 spreads each group over 8/G XCDs (the
+// group's blocks dealt out in longest-first order); any other G falls back
+// to a plain longest-first order.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int wg_count(int groups, int per_group, int nqb) {
+  const int m = per_group * nqb;                     // work-groups of one group
+  if (groups % 8 == 0 || 8 % groups != 0) return groups * m;
+  const int s = 8 / groups;                          // XCDs per group
+  return 8 * ((m + s - 1) / s);
+}
+
+struct WgItem {
+  int b, hk, unit, qb;   // batch entry, KV head, unit of query heads in the group, query block
+  bool valid;
+};
+
+// per_group: work units (sets of query heads) per group.
+__host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int per_group,
+                                          int nqb) {
+  const int groups = batch * n_heads_kv;
+  int g, u, rank;                                    // rank 0 = longest block
+  bool valid = true;
+  if (groups % 8 == 0) {
+    const int x = id & 7, j = id >> 3;
+    const int per_level = (groups >> 3) * per_group;
+    rank = j / per_level;
+    const int r = j - rank * per_level;
+    g = (r / per_group) * 8 + x;
+    u = r % per_group;
+  } else if (8 % groups == 0) {
+    const int s = 8 / groups, x = id & 7, j = id >> 3;
+    g = x % groups;
+    const int i = j * s + x / groups;
+    valid = i < per_group * nqb;
+    rank = i / per_group;
+    u = i % per_group;
+  } else {
+    const int per_level = groups * per_group;
+    rank = id / per_level;
+    const int r = id - rank * per_level;
+    g = r / per_group;
+    u = r % per_group;
+  }
+  WgItem w;
+  w.b = g / n_heads_kv;
+  w.hk = g % n_heads_kv;
+  w.unit = u;
+  w.qb = nqb - 1 - rank;
+  w.valid = valid;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
 // Attention forward.
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, bool UNNORM>
-__global__ void __launch_bounds__(64 * wg_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool BF16, bool UNNORM, int HP>
+__global__ void __launch_bounds__(64 * wg_waves(D, HP)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
-  constexpr int kWaves = wg_waves(D);
+  constexpr int kWaves = wg_waves(D, HP);
   constexpr bool PIPE = D <= 128;            // software-pipelined loop (register budget)
   constexpr int KS = key_split(D);           // waves sharing one query group
-  constexpr int QG = kWaves / KS;            // query groups of 32 rows
+  constexpr int QG = 4;                      // query groups of 32 rows per head
+  static_assert(kWaves == HP * KS * QG, "work-group shape");
   constexpr int kBM = 32 * QG;               // query rows per work-group
   constexpr int BN = tile_keys(D);           // keys per tile
   constexpr int KW = BN / KS;                // keys per wave per tile
@@ -240,12 +303,15 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qw = wave % QG;       // which 32 query rows
-  const int kh = wave / QG;       // which part of every tile
-  const int h = blockIdx.x;
-  const int qb = (int)gridDim.y - 1 - (int)blockIdx.y;   // longest causal rows first
-  const int b = blockIdx.z;
-  const int hk = h / (a.n_heads_q / a.n_heads_kv);
+  const int qw = wave % QG;               // which 32 query rows
+  const int kh = (wave / QG) % KS;        // which part of every tile
+  const int hp = wave / (QG * KS);        // which query head of the work-group
+  const int nqb = (a.seqlen_q + kBM - 1) / kBM;
+  const int per_group = a.n_heads_q / a.n_heads_kv;
+  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nqb);
+  if (!item.valid) return;
+  const int qb = item.qb, b = item.b, hk = item.hk;
+  const int h = hk * per_group + item.unit * HP + hp;   // the launcher picks HP | per_group
   const int q0 = qb * kBM;
   const int off = a.seqlen_kv - a.seqlen_q;              // bottom-right alignment
 
@@ -577,14 +643,25 @@ hipError_t launch_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hipStrea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int BM = block_rows(D);
-  const dim3 grid(a.n_heads_q, (a.seqlen_q + BM - 1) / BM, a.batch);
-  if (unnorm)
-    hipLaunchKernelGGL((prefill_kernel<D, BF16, true>), grid, dim3(64 * wg_waves(D)), 0, stream, a,
-                       (const unsigned short*)w.ws);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, BF16, false>), grid, dim3(64 * wg_waves(D)), 0, stream,
-                       a,
-                       (const unsigned short*)w.ws);
+  const int per_group = a.n_heads_q / a.n_heads_kv;
+  const int nqb = (a.seqlen_q + BM - 1) / BM;
+  const auto go = [&](auto hp_c) {
+    constexpr int HP = decltype(hp_c)::value;
+    const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
+    if (unnorm)
+      hipLaunchKernelGGL((prefill_kernel<D, BF16, true, HP>), grid, dim3(64 * wg_waves(D, HP)), 0,
+                         stream, a, (const unsigned short*)w.ws);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, BF16, false, HP>), grid, dim3(64 * wg_waves(D, HP)),
+                         0, stream, a, (const unsigned short*)w.ws);
+  };
+  if constexpr (D <= 128) {
+    if (per_group % 2 == 0) {
+      go(std::integral_constant<int, 2>{});
+      return hipGetLastError();
+    }
+  }
+  go(std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 

@@ -100,7 +100,7 @@ def _prefill(**kw):
     (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=0.0), 1),
     (dict(scale=-1.0), 1), (dict(q=ALIGNED + 2), 1), (dict(o=ALIGNED + 4), 1),
     (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1), (dict(os=(128, 2, 128)), 1),
-    (dict(ks=(-8, 256, 128)), 1), (dict(Sq=70000 * 128, Skv=70000 * 128), 2),
+    (dict(ks=(-8, 256, 128)), 1), (dict(Sq=2**31 - 1, Skv=2**31 - 1, Hq=128), 2),
     (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(ws=ALIGNED + 16), 1),
 ])
 def test_prefill_validation(kw, status):
