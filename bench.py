@@ -7,8 +7,9 @@ followed by a single-token split-KV decode against a 1641-token fp16 KV cache
 HBM before the timed region.
 
 Prints one JSON line. ``value`` is the prefill's algorithmic throughput in
-TFLOP/s (4 * head_dim FLOPs per visible query/key pair, per query head),
-timed with HIP events on the launch stream. The same line carries the
+TFLOP/s (4 * head_dim FLOPs per visible query/key pair, per query head) over
+both of its launches (V repack + attention), timed with HIP events on the
+launch stream; the roofline entry uses the attention launch alone. The same line carries the
 decode timings, the batched long-context decode (32 sequences, 512..32768
 tokens) and the large-head prefill (head_dim 256, 8192 tokens) as extra
 measurements, a roofline entry per kernel family, and the fp64 CPU oracle's
@@ -52,12 +53,58 @@ def prefill_setup(torch, fa, cfg):
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
     rs = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
 
+    ws = torch.empty(fa.prefill_workspace_size(B, cfg.seqlen_kv, cfg.n_heads_kv, D),
+                     dtype=torch.uint8, device="cuda")
+
+    def pack():
+        fa.prefill_pack_v(v, workspace=ws)
+
+    def attn():
+        fa.prefill_packed(q, k, ws, causal=cfg.causal, softmax_scale=cfg.scale,
+                          out_unnormalized=cfg.out_unnormalized, out=o, lse=lse, row_sum=rs)
+
     def run():
-        fa.prefill(q, k, v, causal=cfg.causal, softmax_scale=cfg.scale,
-                   out_unnormalized=cfg.out_unnormalized, out=o, lse=lse, row_sum=rs)
-    bytes_ = (q.numel() + k.numel() + v.numel()) * 2 + o.numel() * 4 + lse.numel() * 4 * (
-        2 if cfg.out_unnormalized else 1)
-    return run, bytes_
+        pack()
+        attn()
+    return run, pack, attn
+
+
+def prefill_kernel_name(cfg):
+    """The attention kernel's template name as rocprofv3 reports it."""
+    group = cfg.n_heads_q // cfg.n_heads_kv
+    hp = 2 if cfg.head_dim <= 128 and group % 2 == 0 else 1
+    return (f"prefill_kernel<{cfg.head_dim}, {str(cfg.dtype == 'bf16').lower()}, "
+            f"{str(cfg.out_unnormalized).lower()}, {hp}>")
+
+
+def decode_kernel_name(cfg):
+    group = cfg.n_heads_q // cfg.n_heads_kv
+    g = next(x for x in range(8, 0, -1) if group % x == 0)
+    return f"decode_partial_kernel<{cfg.head_dim}, {g}, {str(cfg.dtype == 'bf16').lower()}>"
+
+
+def source_digest(name):
+    """Short digest of a kernel source file: the traffic counters in profiles/
+    apply only to the source they were taken from."""
+    import hashlib
+    path = os.path.join(ROOT, "flashattention_attention_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, source):
+    """HBM bytes per launch (read + write, copy-calibrated) recorded in
+    profiles/hbm_traffic_counters.md for this kernel, workload and source
+    digest, else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+    if not os.path.exists(path):
+        return None
+    import re
+    for line in open(path):
+        m = re.match(r"^traffic kernel=(.+?) workload=(\S+) source=(\S+) read_bytes=(\d+) "
+                     r"write_bytes=(\d+)\s*$", line.strip())
+        if m and m.group(1) == kernel and m.group(2) == workload and m.group(3) == source_digest(source):
+            return int(m.group(4)) + int(m.group(5))
+    return None
 
 
 def decode_setup(torch, fa, cfg, split_len=None):
@@ -155,8 +202,8 @@ def run_profiling_aid(torch, fa, inputs, args):
         label = f"copy {args.copy_bytes} bytes"
     elif args.only in ("prefill", "large_head"):
         cfg = inputs.GQA_PREFILL if args.only == "prefill" else inputs.LARGE_HEAD
-        run, _ = prefill_setup(torch, fa, cfg)
-        fns, label = [run], cfg.name
+        _, pack, attn = prefill_setup(torch, fa, cfg)
+        fns, label = [pack, attn], cfg.name
     else:
         cfg = inputs.GQA_DECODE if args.only == "decode" else inputs.LONG_DECODE
         part, merge, _ = decode_setup(torch, fa, cfg)
@@ -205,7 +252,7 @@ def main():
     print(f"[bench] {props.name} cus={props.multi_processor_count}; preparing inputs",
           file=sys.stderr, flush=True)
 
-    prefill, _ = prefill_setup(torch, fa, pcfg)
+    prefill, p_pack, p_attn = prefill_setup(torch, fa, pcfg)
     d_partial, d_merge, dinfo = decode_setup(torch, fa, dcfg)
 
     def step():
@@ -218,37 +265,45 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [_events(torch, 4) for _ in range(K)]
+    evs = [_events(torch, 5) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         e = evs[i]
         e[0].record()
-        prefill()
+        p_pack()
         e[1].record()
-        d_partial()
+        p_attn()
         e[2].record()
-        d_merge()
+        d_partial()
         e[3].record()
+        d_merge()
+        e[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    part_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    pack_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pre_ms = [a + b for a, b in zip(pack_ms, attn_ms)]
+    part_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    merge_ms = [e[3].elapsed_time(e[4]) for e in evs]
     pre_mean = statistics.mean(pre_ms)
+    attn_mean = statistics.mean(attn_ms)
     flops = pcfg.flops()
     value = flops / (pre_mean * 1e-3) / 1e12
+    attn_tflops = flops / (attn_mean * 1e-3) / 1e12
     dec_us = (statistics.mean(part_ms) + statistics.mean(merge_ms)) * 1e3
     print(f"[bench] timed {K} steps: prefill {pre_mean * 1e3:.1f} us, decode "
           f"{dec_us:.1f} us", file=sys.stderr, flush=True)
 
+    pk = prefill_kernel_name(pcfg)
     rooflines = {
-        "prefill_gqa_s3314": {"bound": "mfma", "achieved": round(value, 2),
+        "prefill_gqa_s3314": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                               "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                              "frac": round(value / MI355X_BF16_DENSE_TFLOPS, 4),
-                              "traffic": None,
-                              "kernel": "prefill_kernel<128,64,bf16>",
-                              "per_launch": f"{flops / 1e9:.2f} GFLOP"}}
+                              "frac": round(attn_tflops / MI355X_BF16_DENSE_TFLOPS, 4),
+                              "traffic": measured_traffic(pk, pcfg.name, "fa_prefill.hip"),
+                              "kernel": pk, "us_per_launch": round(attn_mean * 1e3, 2),
+                              "per_launch": f"{flops / 1e9:.2f} GFLOP (4 * head_dim per "
+                                            f"visible query/key pair and query head)"}}
     line = {
         "metric": "causal GQA prefill attention TFLOP/s (3314 tokens, 28/4 heads, hd 128, bf16)",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
@@ -259,6 +314,8 @@ def main():
                    "seq_len": pcfg.seqlen_q, "kv_len_decode": 1641, "parallelism": "none"},
         "prefill": {"us_per_call": round(pre_mean * 1e3, 2),
                     "us_min": round(min(pre_ms) * 1e3, 2), "gflop": round(flops / 1e9, 3),
+                    "v_repack_us": round(statistics.mean(pack_ms) * 1e3, 2),
+                    "attention_us": round(attn_mean * 1e3, 2),
                     "frac_mfma_peak": round(value / MI355X_BF16_DENSE_TFLOPS, 4)},
         "decode_gqa_kv1641": {
             "split_len": dinfo["split_len"], "max_splits": dinfo["max_splits"],
@@ -317,29 +374,37 @@ def main():
                                    4),
             "partial_bytes_overhead_gb": round(linfo["partial_bytes"] / 1e9, 4),
             "cache": "flushed (512 MB write) before every call"}
+        dk = decode_kernel_name(lcfg)
         rooflines["decode_partial_batched_long"] = {
             "bound": "hbm", "achieved": round(part_gbps, 1), "peak": MI355X_HBM_GBPS,
-            "unit": "GB/s", "frac": round(part_gbps / MI355X_HBM_GBPS, 4), "traffic": None,
-            "kernel": "decode_partial_kernel<128,4,f16>",
-            "per_launch": f"{linfo['kv_bytes'] / 1e9:.4f} GB of K+V"}
+            "unit": "GB/s", "frac": round(part_gbps / MI355X_HBM_GBPS, 4),
+            "traffic": measured_traffic(dk, lcfg.name, "fa_decode.hip"), "kernel": dk,
+            "us_per_launch": round(r[0]["median_ms"] * 1e3, 1),
+            "per_launch": f"{linfo['kv_bytes'] / 1e9:.4f} GB of K+V (each cached key and value "
+                          f"row read once)"}
         del l_partial, l_merge
         torch.cuda.empty_cache()
         print("[bench] large-head prefill", file=sys.stderr, flush=True)
 
         hcfg = inputs.LARGE_HEAD
-        h_run, _ = prefill_setup(torch, fa, hcfg)
+        h_run, h_pack, h_attn = prefill_setup(torch, fa, hcfg)
         h_run()
-        r = time_calls(torch, [h_run], 5)
+        r = time_calls(torch, [h_pack, h_attn], 5)
         hf = hcfg.flops()
-        ht = hf / (r[0]["mean_ms"] * 1e-3) / 1e12
+        h_ms = r[0]["mean_ms"] + r[1]["mean_ms"]
+        ht = hf / (h_ms * 1e-3) / 1e12
+        ha = hf / (r[1]["mean_ms"] * 1e-3) / 1e12
         line["prefill_large_head"] = {"workload": hcfg.name,
-                                      "us_per_call": round(r[0]["mean_ms"] * 1e3, 1),
+                                      "us_per_call": round(h_ms * 1e3, 1),
+                                      "attention_us": round(r[1]["mean_ms"] * 1e3, 1),
                                       "tflops": round(ht, 2),
                                       "frac_mfma_peak": round(ht / MI355X_BF16_DENSE_TFLOPS, 4)}
+        hk = prefill_kernel_name(hcfg)
         rooflines["prefill_large_head"] = {
-            "bound": "mfma", "achieved": round(ht, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ht / MI355X_BF16_DENSE_TFLOPS, 4),
-            "traffic": None, "kernel": "prefill_kernel<256,32,bf16,unnormalized>",
+            "bound": "mfma", "achieved": round(ha, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ha / MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": measured_traffic(hk, hcfg.name, "fa_prefill.hip"), "kernel": hk,
+            "us_per_launch": round(r[1]["mean_ms"] * 1e3, 1),
             "per_launch": f"{hf / 1e12:.4f} TFLOP"}
         del flush_buf
 

@@ -38,6 +38,88 @@ int hip_status(hipError_t e, const char* what) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Query/key/output side of a prefill call.
+int check_attn(const char* fn, const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+               const void* k, int64_t k_sb, int64_t k_ss, int64_t k_sh, const float* o,
+               int64_t o_sb, int64_t o_ss, int64_t o_sh, const float* lse,
+               const float* row_sum, int batch, int seqlen_q, int seqlen_kv, int n_heads_q,
+               int n_heads_kv, int head_dim, int dtype, float softmax_scale,
+               int out_unnormalized) {
+  if (!q || !k || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "%s: q, k, v, o and lse must be non-null", fn);
+  if (out_unnormalized && !row_sum)
+    return fail(FA_ERR_INVALID_ARG, "%s: row_sum is required with out_unnormalized", fn);
+  if (batch < 1 || seqlen_q < 1 || n_heads_q < 1 || n_heads_kv < 1)
+    return fail(FA_ERR_INVALID_ARG, "%s: batch, seqlen_q and head counts must be >= 1", fn);
+  if (seqlen_kv < seqlen_q)
+    return fail(FA_ERR_INVALID_ARG, "%s: seqlen_kv (%d) < seqlen_q (%d)", fn, seqlen_kv,
+                seqlen_q);
+  if (n_heads_q % n_heads_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "%s: n_heads_q (%d) %% n_heads_kv (%d) != 0", fn, n_heads_q,
+                n_heads_kv);
+  if (!head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F16 or FA_BF16", fn, dtype);
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(o))
+    return fail(FA_ERR_INVALID_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
+  const int64_t hs[6] = {q_sb, q_ss, q_sh, k_sb, k_ss, k_sh};
+  for (int i = 0; i < 6; ++i)
+    if (hs[i] < 0 || hs[i] % 8 != 0)
+      return fail(FA_ERR_INVALID_ARG,
+                  "%s: q/k/v strides must be non-negative multiples of 8 elements", fn);
+  if (o_sb < 0 || o_ss < 0 || o_sh < 0 || o_sb % 4 || o_ss % 4 || o_sh % 4)
+    return fail(FA_ERR_INVALID_ARG, "%s: o strides must be non-negative multiples of 4 elements",
+                fn);
+  if ((int64_t)batch * n_heads_q * ((seqlen_q + 127) / 128) > (1 << 30))
+    return fail(FA_ERR_UNSUPPORTED, "%s: grid too large (seqlen_q, heads or batch)", fn);
+  if (k_ss > (int64_t)(1 << 23))
+    return fail(FA_ERR_UNSUPPORTED, "%s: k sequence stride above 2^23 elements", fn);
+  return FA_OK;
+}
+
+// Value side of a prefill call (the tensor repacked into the workspace).
+int check_pack(const char* fn, const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh) {
+  if (!v) return fail(FA_ERR_INVALID_ARG, "%s: q, k, v, o and lse must be non-null", fn);
+  if (!aligned16(v)) return fail(FA_ERR_INVALID_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
+  const int64_t hs[3] = {v_sb, v_ss, v_sh};
+  for (int i = 0; i < 3; ++i)
+    if (hs[i] < 0 || hs[i] % 8 != 0)
+      return fail(FA_ERR_INVALID_ARG,
+                  "%s: q/k/v strides must be non-negative multiples of 8 elements", fn);
+  return FA_OK;
+}
+
+int check_workspace(const char* fn, const void* workspace, uint64_t workspace_bytes, int batch,
+                    int seqlen_kv, int n_heads_kv, int head_dim) {
+  const uint64_t need = fa::prefill_workspace_bytes(batch, seqlen_kv, n_heads_kv, head_dim);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(FA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned and hold %llu bytes",
+                fn, (unsigned long long)need);
+  return FA_OK;
+}
+
+fa::PrefillArgs prefill_args(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                             const void* k, int64_t k_sb, int64_t k_ss, int64_t k_sh,
+                             const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh, float* o,
+                             int64_t o_sb, int64_t o_ss, int64_t o_sh, float* lse,
+                             float* row_sum, int batch, int seqlen_q, int seqlen_kv,
+                             int n_heads_q, int n_heads_kv, int causal, float softmax_scale) {
+  fa::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_sum = row_sum;
+  a.q_sb = q_sb; a.q_ss = q_ss; a.q_sh = q_sh;
+  a.k_sb = k_sb; a.k_ss = k_ss; a.k_sh = k_sh;
+  a.v_sb = v_sb; a.v_ss = v_ss; a.v_sh = v_sh;
+  a.o_sb = o_sb; a.o_ss = o_ss; a.o_sh = o_sh;
+  a.batch = batch; a.seqlen_q = seqlen_q; a.seqlen_kv = seqlen_kv;
+  a.n_heads_q = n_heads_q; a.n_heads_kv = n_heads_kv;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,60 +145,72 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                    int head_dim, int dtype, int causal, float softmax_scale,
                    int out_unnormalized, void* workspace, uint64_t workspace_bytes,
                    void* stream) {
-  if (!q || !k || !v || !o || !lse)
-    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: q, k, v, o and lse must be non-null");
-  if (out_unnormalized && !row_sum)
-    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: row_sum is required with out_unnormalized");
-  if (batch < 1 || seqlen_q < 1 || n_heads_q < 1 || n_heads_kv < 1)
-    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: batch, seqlen_q and head counts must be >= 1");
-  if (seqlen_kv < seqlen_q)
-    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: seqlen_kv (%d) < seqlen_q (%d)", seqlen_kv,
-                seqlen_q);
-  if (n_heads_q % n_heads_kv != 0)
-    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: n_heads_q (%d) %% n_heads_kv (%d) != 0",
-                n_heads_q, n_heads_kv);
-  if (!head_dim_supported(head_dim))
-    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: head_dim %d not in {64, 128, 256}", head_dim);
-  if (dtype != FA_F16 && dtype != FA_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: dtype %d is not FA_F16 or FA_BF16", dtype);
-  if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
-    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: softmax_scale must be finite and > 0");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(FA_ERR_INVALID_ARG, "fa_prefill_fwd: q, k, v, o must be 16-byte aligned");
-  const int64_t hs[9] = {q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh};
-  for (int i = 0; i < 9; ++i)
-    if (hs[i] < 0 || hs[i] % 8 != 0)
-      return fail(FA_ERR_INVALID_ARG,
-                  "fa_prefill_fwd: q/k/v strides must be non-negative multiples of 8 elements");
-  if (o_sb < 0 || o_ss < 0 || o_sh < 0 || o_sb % 4 || o_ss % 4 || o_sh % 4)
-    return fail(FA_ERR_INVALID_ARG,
-                "fa_prefill_fwd: o strides must be non-negative multiples of 4 elements");
-  if ((int64_t)batch * n_heads_q * ((seqlen_q + 127) / 128) > (1 << 30))
-    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: grid too large (seqlen_q or batch)");
-  if (k_ss > (int64_t)(1 << 23))
-    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: k sequence stride above 2^23 elements");
-  const uint64_t need = fa::prefill_workspace_bytes(batch, seqlen_kv, n_heads_kv, head_dim);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
-    return fail(FA_ERR_INVALID_ARG,
-                "fa_prefill_fwd: workspace must be 256-byte aligned and hold %llu bytes",
-                (unsigned long long)need);
+  const char* fn = "fa_prefill_fwd";
+  int st = check_attn(fn, q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, o, o_sb, o_ss, o_sh, lse,
+                      row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, dtype,
+                      softmax_scale, out_unnormalized);
+  if (st == FA_OK) st = check_pack(fn, v, v_sb, v_ss, v_sh);
+  if (st == FA_OK)
+    st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
+  if (st != FA_OK) return st;
+  const fa::PrefillArgs a =
+      prefill_args(q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, v, v_sb, v_ss, v_sh, o, o_sb, o_ss,
+                   o_sh, lse, row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, causal,
+                   softmax_scale);
+  const fa::VtArgs w{workspace, (size_t)workspace_bytes};
+  const hipError_t e =
+      fa::launch_prefill_pack(a, w, head_dim, dtype == FA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "fa_prefill_fwd V repack launch");
+  return hip_status(fa::launch_prefill_attn(a, w, head_dim, dtype == FA_BF16,
+                                            out_unnormalized != 0, (hipStream_t)stream),
+                    "fa_prefill_fwd attention launch");
+}
 
-  fa::PrefillArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_sum = row_sum;
-  a.q_sb = q_sb; a.q_ss = q_ss; a.q_sh = q_sh;
-  a.k_sb = k_sb; a.k_ss = k_ss; a.k_sh = k_sh;
-  a.v_sb = v_sb; a.v_ss = v_ss; a.v_sh = v_sh;
-  a.o_sb = o_sb; a.o_ss = o_ss; a.o_sh = o_sh;
-  a.batch = batch; a.seqlen_q = seqlen_q; a.seqlen_kv = seqlen_kv;
-  a.n_heads_q = n_heads_q; a.n_heads_kv = n_heads_kv;
-  a.causal = causal ? 1 : 0;
-  a.scale_log2 = softmax_scale * kLog2e;
-  fa::VtArgs w;
-  w.ws = workspace;
-  w.bytes = workspace_bytes;
-  return hip_status(fa::launch_prefill(a, w, head_dim, dtype == FA_BF16, out_unnormalized != 0,
-                                       (hipStream_t)stream),
-                    "fa_prefill_fwd launch");
+int fa_prefill_pack_v(const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh, int batch,
+                      int seqlen_kv, int n_heads_kv, int head_dim, int dtype, void* workspace,
+                      uint64_t workspace_bytes, void* stream) {
+  const char* fn = "fa_prefill_pack_v";
+  if (batch < 1 || seqlen_kv < 1 || n_heads_kv < 1)
+    return fail(FA_ERR_INVALID_ARG, "%s: batch, seqlen_kv and n_heads_kv must be >= 1", fn);
+  if (!head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F16 or FA_BF16", fn, dtype);
+  int st = check_pack(fn, v, v_sb, v_ss, v_sh);
+  if (st == FA_OK)
+    st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
+  if (st != FA_OK) return st;
+  fa::PrefillArgs a{};
+  a.v = v; a.v_sb = v_sb; a.v_ss = v_ss; a.v_sh = v_sh;
+  a.batch = batch; a.seqlen_kv = seqlen_kv; a.n_heads_kv = n_heads_kv;
+  const fa::VtArgs w{workspace, (size_t)workspace_bytes};
+  return hip_status(fa::launch_prefill_pack(a, w, head_dim, dtype == FA_BF16, (hipStream_t)stream),
+                    "fa_prefill_pack_v launch");
+}
+
+int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                          const void* k, int64_t k_sb, int64_t k_ss, int64_t k_sh,
+                          float* o, int64_t o_sb, int64_t o_ss, int64_t o_sh,
+                          float* lse, float* row_sum,
+                          int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                          int head_dim, int dtype, int causal, float softmax_scale,
+                          int out_unnormalized, const void* workspace, uint64_t workspace_bytes,
+                          void* stream) {
+  const char* fn = "fa_prefill_fwd_packed";
+  int st = check_attn(fn, q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, o, o_sb, o_ss, o_sh, lse,
+                      row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, dtype,
+                      softmax_scale, out_unnormalized);
+  if (st == FA_OK)
+    st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
+  if (st != FA_OK) return st;
+  const fa::PrefillArgs a =
+      prefill_args(q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, nullptr, 0, 0, 0, o, o_sb, o_ss,
+                   o_sh, lse, row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, causal,
+                   softmax_scale);
+  const fa::VtArgs w{const_cast<void*>(workspace), (size_t)workspace_bytes};
+  return hip_status(fa::launch_prefill_attn(a, w, head_dim, dtype == FA_BF16,
+                                            out_unnormalized != 0, (hipStream_t)stream),
+                    "fa_prefill_fwd_packed launch");
 }
 
 uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int head_dim) {

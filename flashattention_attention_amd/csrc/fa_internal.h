@@ -57,8 +57,12 @@ struct VtArgs {
 size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int head_dim);
 
 // Launchers: enqueue on `stream`, return the launch's hipError_t.
-hipError_t launch_prefill(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
-                          bool unnormalized, hipStream_t stream);
+// Prefill in two launches: V -> fp16 V^T tiles in the workspace (uses a.v and
+// its strides), then attention reading the V^T tiles from the workspace.
+hipError_t launch_prefill_pack(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
+                               hipStream_t stream);
+hipError_t launch_prefill_attn(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
+                               bool unnormalized, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                                  hipStream_t stream);
 hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

@@ -633,15 +633,18 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
 }
 
 template <int D, bool BF16>
-hipError_t launch_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hipStream_t stream) {
+hipError_t launch_pack_d(const PrefillArgs& a, const VtArgs& w, hipStream_t stream) {
   constexpr int BN = tile_keys(D);
   const int ntiles = (a.seqlen_kv + BN - 1) / BN;
   const int units = ntiles * (BN / 8) * (D / 8);
   hipLaunchKernelGGL((vt_pack_kernel<D, BF16>), dim3((units + 255) / 256, a.n_heads_kv, a.batch),
                      dim3(256), 0, stream, (const unsigned short*)a.v, a.v_sb, a.v_ss, a.v_sh,
                      a.seqlen_kv, a.n_heads_kv, ntiles, (unsigned short*)w.ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_attn_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hipStream_t stream) {
   constexpr int BM = block_rows(D);
   const int per_group = a.n_heads_q / a.n_heads_kv;
   const int nqb = (a.seqlen_q + BM - 1) / BM;
@@ -673,18 +676,28 @@ size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int hea
   return (size_t)batch * n_heads_kv * ntiles * bn * head_dim * 2;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
-                          bool unnormalized, hipStream_t stream) {
+hipError_t launch_prefill_pack(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
+                               hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return bf16 ? launch_pack_d<64, true>(a, w, stream) : launch_pack_d<64, false>(a, w, stream);
+    case 128: return bf16 ? launch_pack_d<128, true>(a, w, stream) : launch_pack_d<128, false>(a, w, stream);
+    case 256: return bf16 ? launch_pack_d<256, true>(a, w, stream) : launch_pack_d<256, false>(a, w, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill_attn(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
+                               bool unnormalized, hipStream_t stream) {
   switch (head_dim) {
     case 64:
-      return bf16 ? launch_d<64, true>(a, w, unnormalized, stream)
-                  : launch_d<64, false>(a, w, unnormalized, stream);
+      return bf16 ? launch_attn_d<64, true>(a, w, unnormalized, stream)
+                  : launch_attn_d<64, false>(a, w, unnormalized, stream);
     case 128:
-      return bf16 ? launch_d<128, true>(a, w, unnormalized, stream)
-                  : launch_d<128, false>(a, w, unnormalized, stream);
+      return bf16 ? launch_attn_d<128, true>(a, w, unnormalized, stream)
+                  : launch_attn_d<128, false>(a, w, unnormalized, stream);
     case 256:
-      return bf16 ? launch_d<256, true>(a, w, unnormalized, stream)
-                  : launch_d<256, false>(a, w, unnormalized, stream);
+      return bf16 ? launch_attn_d<256, true>(a, w, unnormalized, stream)
+                  : launch_attn_d<256, false>(a, w, unnormalized, stream);
     default:
       return hipErrorInvalidValue;
   }

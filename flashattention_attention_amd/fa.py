@@ -30,6 +30,12 @@ _SIGNATURES = {
                         _vp, _i64, _i64, _i64, _vp, _vp,
                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, ctypes.c_uint64, _vp], _i32),
+    "fa_prefill_pack_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                           _vp, ctypes.c_uint64, _vp], _i32),
+    "fa_prefill_fwd_packed": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                               _vp, _i64, _i64, _i64, _vp, _vp,
+                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                               _vp, ctypes.c_uint64, _vp], _i32),
     "fa_prefill_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
     "fa_decode_plan": ([ctypes.POINTER(ctypes.c_int32), _i32, _i32, _i32, _i32, _i32,
                         ctypes.POINTER(_i32), ctypes.POINTER(_i32)], _i32),
@@ -113,6 +119,45 @@ def _default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
 
 
+def _prefill_outputs(q, k, dev, out, lse, row_sum, out_unnormalized, want_row_sum):
+    if q.dim() != 4 or k.dim() != 4:
+        raise FAError("q, k, v must be 4-D [batch, seq, heads, head_dim]")
+    if q.dtype != k.dtype:
+        raise FAError("q, k, v must share a dtype")
+    for t in (q, k):
+        if t.stride(3) != 1:
+            raise FAError("head_dim must be the contiguous dimension")
+    B, Sq, Hq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise FAError("q and k disagree on batch or head_dim")
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    need_rs = out_unnormalized or want_row_sum or row_sum is not None
+    if need_rs and row_sum is None:
+        row_sum = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    _on_gpu(out, lse, *([row_sum] if row_sum is not None else []))
+    if out.dtype != torch.float32 or out.shape != (B, Sq, Hq, D) or out.stride(3) != 1:
+        raise FAError("out must be fp32 [B,Sq,Hq,D] with contiguous head_dim")
+    for t in (lse, row_sum):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, Hq, Sq)
+                              or not t.is_contiguous()):
+            raise FAError("lse / row_sum must be contiguous fp32 [B,Hq,Sq]")
+    return out, lse, row_sum, need_rs
+
+
+def _workspace(k, dev, workspace):
+    B, Skv, Hkv, D = k.shape
+    ws_need = load_library().fa_prefill_workspace_size(B, Skv, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    _on_gpu(workspace)
+    if workspace.numel() * workspace.element_size() < ws_need:
+        raise FAError(f"workspace holds {workspace.numel()} bytes, {ws_need} needed")
+    return workspace
+
+
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True,
             softmax_scale: Optional[float] = None, out_unnormalized: bool = False,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -128,42 +173,17 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
     row_sum are fp32 [B,Hq,Sq].
     """
     dev = _on_gpu(q, k, v)
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise FAError("q, k, v must be 4-D [batch, seq, heads, head_dim]")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise FAError("q, k, v must share a dtype")
-    if k.shape != v.shape:
-        raise FAError("k and v must have the same shape")
-    for t in (q, k, v):
-        if t.stride(3) != 1:
-            raise FAError("head_dim must be the contiguous dimension")
+    if v.dim() != 4 or k.shape != v.shape or v.dtype != k.dtype:
+        raise FAError("k and v must have the same shape and dtype")
+    if v.stride(3) != 1:
+        raise FAError("head_dim must be the contiguous dimension")
+    out, lse, row_sum, need_rs = _prefill_outputs(q, k, dev, out, lse, row_sum,
+                                                  out_unnormalized, want_row_sum)
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
-    if k.shape[0] != B or k.shape[3] != D:
-        raise FAError("q and k disagree on batch or head_dim")
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
-    if out is None:
-        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
-    need_rs = out_unnormalized or want_row_sum or row_sum is not None
-    if need_rs and row_sum is None:
-        row_sum = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
-    _on_gpu(out, lse, *([row_sum] if row_sum is not None else []))
-    if out.dtype != torch.float32 or out.shape != (B, Sq, Hq, D) or out.stride(3) != 1:
-        raise FAError("out must be fp32 [B,Sq,Hq,D] with contiguous head_dim")
-    for t in (lse, row_sum):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (B, Hq, Sq)
-                              or not t.is_contiguous()):
-            raise FAError("lse / row_sum must be contiguous fp32 [B,Hq,Sq]")
-    lib = load_library()
-    ws_need = lib.fa_prefill_workspace_size(B, Skv, Hkv, D)
-    if workspace is None:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
-    _on_gpu(workspace)
-    if workspace.numel() * workspace.element_size() < ws_need:
-        raise FAError(f"workspace holds {workspace.numel()} bytes, {ws_need} needed")
-    st = lib.fa_prefill_fwd(
+    workspace = _workspace(k, dev, workspace)
+    st = load_library().fa_prefill_fwd(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
         v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
@@ -173,6 +193,44 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
         1 if out_unnormalized else 0, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st, "fa_prefill_fwd")
+    return (out, lse, row_sum) if need_rs else (out, lse)
+
+
+def prefill_pack_v(v: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Repack V [B,Skv,Hkv,D] into a prefill workspace (returned) for prefill_packed."""
+    dev = _on_gpu(v)
+    if v.dim() != 4 or v.stride(3) != 1:
+        raise FAError("v must be 4-D [batch, seq, heads, head_dim] with contiguous head_dim")
+    workspace = _workspace(v, dev, workspace)
+    B, Skv, Hkv, D = v.shape
+    st = load_library().fa_prefill_pack_v(
+        v.data_ptr(), v.stride(0), v.stride(1), v.stride(2), B, Skv, Hkv, D, _dtype_code(v),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "fa_prefill_pack_v")
+    return workspace
+
+
+def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
+                   causal: bool = True, softmax_scale: Optional[float] = None,
+                   out_unnormalized: bool = False, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, row_sum: Optional[torch.Tensor] = None,
+                   want_row_sum: bool = False):
+    """prefill() with V taken from a workspace filled by prefill_pack_v (same shapes)."""
+    dev = _on_gpu(q, k, packed_v)
+    out, lse, row_sum, need_rs = _prefill_outputs(q, k, dev, out, lse, row_sum,
+                                                  out_unnormalized, want_row_sum)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
+    st = load_library().fa_prefill_fwd_packed(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
+        B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
+        1 if out_unnormalized else 0, packed_v.data_ptr(),
+        packed_v.numel() * packed_v.element_size(), _stream(dev))
+    _check(st, "fa_prefill_fwd_packed")
     return (out, lse, row_sum) if need_rs else (out, lse)
 
 

@@ -104,6 +104,39 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                    void* stream);
 
 /*
+ * fa_prefill_pack_v / fa_prefill_fwd_packed — fa_prefill_fwd in its two
+ * launches, for callers that attend several query sets to one V (a cached
+ * prefix) or that time the attention kernel on its own.
+ *
+ * Source: as fa_prefill_fwd; the V^T tile layout is the operand order of the
+ * P.V product of "STAGE_D.md — FMHA Kernel Development", "Kernel Output".
+ *
+ * fa_prefill_pack_v writes V (layout and strides as in fa_prefill_fwd) into
+ * `workspace` as fp16 V^T tiles; nothing else is read or written.
+ * fa_prefill_fwd_packed then takes the same arguments as fa_prefill_fwd minus
+ * v and its strides, and reads V from a workspace that a completed or
+ * earlier-enqueued fa_prefill_pack_v call filled for the same batch,
+ * seqlen_kv, n_heads_kv and head_dim (dtype of q/k may differ from the packed
+ * V's). The workspace is only read by fa_prefill_fwd_packed, so any number of
+ * calls may share one packed workspace; a pack into it must not overlap them
+ * in time. Using a workspace that was not filled this way gives unspecified
+ * (finite or not) outputs but no out-of-bounds access. Validation and errors
+ * as in fa_prefill_fwd; fa_prefill_pack_v checks only its own arguments.
+ */
+int fa_prefill_pack_v(const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh, int batch,
+                      int seqlen_kv, int n_heads_kv, int head_dim, int dtype, void* workspace,
+                      uint64_t workspace_bytes, void* stream);
+
+int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                          const void* k, int64_t k_sb, int64_t k_ss, int64_t k_sh,
+                          float* o, int64_t o_sb, int64_t o_ss, int64_t o_sh,
+                          float* lse, float* row_sum,
+                          int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                          int head_dim, int dtype, int causal, float softmax_scale,
+                          int out_unnormalized, const void* workspace, uint64_t workspace_bytes,
+                          void* stream);
+
+/*
  * fa_prefill_workspace_size — bytes of workspace fa_prefill_fwd needs
  * (batch * n_heads_kv * ceil(seqlen_kv / 64) * head_dim * 64 * 2). Returns 0
  * for non-positive sizes. Host only; never fails otherwise.

@@ -22,7 +22,8 @@ def _gpu_visible():
 
 def test_exports_every_declared_symbol():
     names = fa.declared_functions()
-    assert set(names) == {"fa_prefill_fwd", "fa_prefill_workspace_size", "fa_decode_plan",
+    assert set(names) == {"fa_prefill_fwd", "fa_prefill_pack_v", "fa_prefill_fwd_packed",
+                          "fa_prefill_workspace_size", "fa_decode_plan",
                           "fa_decode_split_partial", "fa_decode_merge_lse", "fa_status_string",
                           "fa_last_error"}
     lib = ctypes.CDLL(fa.library_path())
@@ -107,6 +108,42 @@ def test_prefill_validation(kw, status):
     st = _prefill(**kw)
     assert st == status, fa.load_library().fa_last_error()
     assert fa.load_library().fa_last_error() != b""
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
+@pytest.mark.parametrize("kw,status", [
+    (dict(v=None), 1), (dict(B=0), 1), (dict(Skv=0), 1), (dict(D=96), 2), (dict(dtype=3), 2),
+    (dict(v=ALIGNED + 2), 1), (dict(vs=(128 * 2 * 128, 2 * 128 + 4, 128)), 1),
+    (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(ws=ALIGNED + 64), 1),
+])
+def test_prefill_pack_v_validation(kw, status):
+    b = dict(v=ALIGNED, vs=(128 * 2 * 128, 2 * 128, 128), B=1, Skv=128, Hkv=2, D=128, dtype=0,
+             ws=ALIGNED, wsb=1 << 40)
+    b.update(kw)
+    lib = fa.load_library()
+    st = lib.fa_prefill_pack_v(b["v"], *b["vs"], b["B"], b["Skv"], b["Hkv"], b["D"], b["dtype"],
+                               b["ws"], b["wsb"], None)
+    assert st == status, lib.fa_last_error()
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(lse=None), 1), (dict(unnorm=1), 1),
+    (dict(Skv=64), 1), (dict(Hkv=3), 1), (dict(D=512), 2), (dict(scale=0.0), 1),
+    (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1),
+])
+def test_prefill_fwd_packed_validation(kw, status):
+    b = dict(q=ALIGNED, k=ALIGNED, o=ALIGNED, lse=ALIGNED, row_sum=None, B=1, Sq=128, Skv=128,
+             Hq=4, Hkv=2, D=128, dtype=0, causal=1, scale=0.125, unnorm=0,
+             qs=(128 * 4 * 128, 4 * 128, 128), ks=(128 * 2 * 128, 2 * 128, 128),
+             os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40)
+    b.update(kw)
+    lib = fa.load_library()
+    st = lib.fa_prefill_fwd_packed(b["q"], *b["qs"], b["k"], *b["ks"], b["o"], *b["os"],
+                                   b["lse"], b["row_sum"], b["B"], b["Sq"], b["Skv"], b["Hq"],
+                                   b["Hkv"], b["D"], b["dtype"], b["causal"], b["scale"],
+                                   b["unnorm"], b["ws"], b["wsb"], None)
+    assert st == status, lib.fa_last_error()
 
 
 @pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
