@@ -162,14 +162,16 @@ __device__ __forceinline__ int vt_chunk_offset(int d, int c) {
 // V -> fp16 V^T tiles. One thread transposes 8 keys x 8 dims: the 8 keys of
 // one chunk (see vt_chunk_offset) for dims d0 .. d0+7.
 // ---------------------------------------------------------------------------
+constexpr int kPackThreads = 64;   // one wave per work-group: a few hundred of them fill the chip
+
 template <int D, bool BF16>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kPackThreads)
 vt_pack_kernel(const unsigned short* __restrict__ v, int64_t v_sb, int64_t v_ss, int64_t v_sh,
                int seqlen_kv, int n_heads_kv, int ntiles, unsigned short* __restrict__ ws) {
   constexpr int BN = tile_keys(D);
   constexpr int NCH = BN / 8;                        // chunks per V^T row
   constexpr int UNITS = NCH * (D / 8);               // (chunk, dim-group) units per tile
-  const int u = blockIdx.x * 256 + threadIdx.x;
+  const int u = blockIdx.x * kPackThreads + threadIdx.x;
   const int t = u / UNITS;
   if (t >= ntiles) return;
   const int c = (u % UNITS) % NCH;                   // chunk: its 8 keys
@@ -637,8 +639,9 @@ hipError_t launch_pack_d(const PrefillArgs& a, const VtArgs& w, hipStream_t stre
   constexpr int BN = tile_keys(D);
   const int ntiles = (a.seqlen_kv + BN - 1) / BN;
   const int units = ntiles * (BN / 8) * (D / 8);
-  hipLaunchKernelGGL((vt_pack_kernel<D, BF16>), dim3((units + 255) / 256, a.n_heads_kv, a.batch),
-                     dim3(256), 0, stream, (const unsigned short*)a.v, a.v_sb, a.v_ss, a.v_sh,
+  hipLaunchKernelGGL((vt_pack_kernel<D, BF16>),
+                     dim3((units + kPackThreads - 1) / kPackThreads, a.n_heads_kv, a.batch),
+                     dim3(kPackThreads), 0, stream, (const unsigned short*)a.v, a.v_sb, a.v_ss, a.v_sh,
                      a.seqlen_kv, a.n_heads_kv, ntiles, (unsigned short*)w.ws);
   return hipGetLastError();
 }
