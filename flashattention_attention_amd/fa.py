@@ -91,6 +91,22 @@ def _check(status: int, what: str) -> None:
                       f"{lib.fa_last_error().decode()}", status)
 
 
+def _issue(name: str, args: tuple, keep: tuple, prepare: bool):
+    """Call the library entry `name` with marshalled `args`, or (prepare=True)
+    return a zero-argument callable that re-issues exactly this call: the
+    tensors in `keep` stay referenced by it, and no Python-side checks run per
+    call (for launch loops where host overhead would starve the GPU)."""
+    fn = getattr(load_library(), name)
+    if prepare:
+        def call(fn=fn, args=args, keep=keep):
+            st = fn(*args)
+            if st != FA_OK:
+                _check(st, name)
+        return call
+    _check(fn(*args), name)
+    return None
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float16:
         return FA_F16
@@ -196,41 +212,46 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
     return (out, lse, row_sum) if need_rs else (out, lse)
 
 
-def prefill_pack_v(v: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Repack V [B,Skv,Hkv,D] into a prefill workspace (returned) for prefill_packed."""
+def prefill_pack_v(v: torch.Tensor, workspace: Optional[torch.Tensor] = None, *,
+                   prepare: bool = False):
+    """Repack V [B,Skv,Hkv,D] into a prefill workspace (returned) for prefill_packed.
+    With prepare=True, returns a callable that repeats the call instead."""
     dev = _on_gpu(v)
     if v.dim() != 4 or v.stride(3) != 1:
         raise FAError("v must be 4-D [batch, seq, heads, head_dim] with contiguous head_dim")
     workspace = _workspace(v, dev, workspace)
     B, Skv, Hkv, D = v.shape
-    st = load_library().fa_prefill_pack_v(
+    call = _issue("fa_prefill_pack_v", (
         v.data_ptr(), v.stride(0), v.stride(1), v.stride(2), B, Skv, Hkv, D, _dtype_code(v),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(st, "fa_prefill_pack_v")
-    return workspace
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)),
+        (v, workspace), prepare)
+    return call if prepare else workspace
 
 
 def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
                    causal: bool = True, softmax_scale: Optional[float] = None,
                    out_unnormalized: bool = False, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, row_sum: Optional[torch.Tensor] = None,
-                   want_row_sum: bool = False):
-    """prefill() with V taken from a workspace filled by prefill_pack_v (same shapes)."""
+                   want_row_sum: bool = False, prepare: bool = False):
+    """prefill() with V taken from a workspace filled by prefill_pack_v (same shapes).
+    With prepare=True, returns a callable that repeats the call (pass the outputs)."""
     dev = _on_gpu(q, k, packed_v)
     out, lse, row_sum, need_rs = _prefill_outputs(q, k, dev, out, lse, row_sum,
                                                   out_unnormalized, want_row_sum)
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
-    st = load_library().fa_prefill_fwd_packed(
+    call = _issue("fa_prefill_fwd_packed", (
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
         B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
         1 if out_unnormalized else 0, packed_v.data_ptr(),
-        packed_v.numel() * packed_v.element_size(), _stream(dev))
-    _check(st, "fa_prefill_fwd_packed")
+        packed_v.numel() * packed_v.element_size(), _stream(dev)),
+        (q, k, packed_v, out, lse, row_sum), prepare)
+    if prepare:
+        return call
     return (out, lse, row_sum) if need_rs else (out, lse)
 
 
@@ -258,8 +279,9 @@ def decode_split_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                          kv_offsets: torch.Tensor, kv_lens: torch.Tensor, *, split_len: int,
                          max_splits: int, softmax_scale: Optional[float] = None,
                          part_o: Optional[torch.Tensor] = None,
-                         part_lse: Optional[torch.Tensor] = None):
+                         part_lse: Optional[torch.Tensor] = None, prepare: bool = False):
     """Split partials. q [B,Hq,D]; caches [T,Hkv,D]; kv_offsets int64 [B]; kv_lens int32 [B].
+    With prepare=True, returns a callable that repeats the call instead.
 
     Returns part_o fp32 [B,Hq,max_splits,D] and part_lse fp32 [B,Hq,max_splits]
     (entries of empty splits are left untouched).
@@ -291,20 +313,20 @@ def decode_split_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
             or part_o.dtype != torch.float32 or part_lse.shape != (B, Hq, max_splits)
             or not part_lse.is_contiguous() or part_lse.dtype != torch.float32):
         raise FAError("part_o / part_lse have the wrong shape, dtype or layout")
-    lib = load_library()
-    st = lib.fa_decode_split_partial(
+    call = _issue("fa_decode_split_partial", (
         q.data_ptr(), q.stride(0), q.stride(1), k_cache.data_ptr(), v_cache.data_ptr(),
         k_cache.stride(0), k_cache.stride(1), kv_offsets.data_ptr(), kv_lens.data_ptr(),
         B, Hq, Hkv, D, _dtype_code(q), scale, split_len, max_splits,
-        part_o.data_ptr(), part_lse.data_ptr(), _stream(dev))
-    _check(st, "fa_decode_split_partial")
-    return part_o, part_lse
+        part_o.data_ptr(), part_lse.data_ptr(), _stream(dev)),
+        (q, k_cache, v_cache, kv_offsets, kv_lens, part_o, part_lse), prepare)
+    return call if prepare else (part_o, part_lse)
 
 
 def decode_merge_lse(part_o: torch.Tensor, part_lse: torch.Tensor, kv_lens: torch.Tensor, *,
                      split_len: int, out: Optional[torch.Tensor] = None,
-                     lse: Optional[torch.Tensor] = None):
-    """Merge partials by LSE. Returns o fp32 [B,Hq,D] and lse fp32 [B,Hq]."""
+                     lse: Optional[torch.Tensor] = None, prepare: bool = False):
+    """Merge partials by LSE. Returns o fp32 [B,Hq,D] and lse fp32 [B,Hq]; with
+    prepare=True, a callable that repeats the call instead."""
     dev = _on_gpu(part_o, part_lse, kv_lens)
     B, Hq, S, D = part_o.shape
     if part_lse.shape != (B, Hq, S) or kv_lens.shape != (B,) or kv_lens.dtype != torch.int32:
@@ -319,12 +341,11 @@ def decode_merge_lse(part_o: torch.Tensor, part_lse: torch.Tensor, kv_lens: torc
     if out.shape != (B, Hq, D) or lse.shape != (B, Hq) or not out.is_contiguous() \
             or not lse.is_contiguous():
         raise FAError("out / lse shape mismatch")
-    lib = load_library()
-    st = lib.fa_decode_merge_lse(part_o.data_ptr(), part_lse.data_ptr(), kv_lens.data_ptr(),
-                                 B, Hq, D, split_len, S, out.data_ptr(), lse.data_ptr(),
-                                 _stream(dev))
-    _check(st, "fa_decode_merge_lse")
-    return out, lse
+    call = _issue("fa_decode_merge_lse", (
+        part_o.data_ptr(), part_lse.data_ptr(), kv_lens.data_ptr(), B, Hq, D, split_len, S,
+        out.data_ptr(), lse.data_ptr(), _stream(dev)), (part_o, part_lse, kv_lens, out, lse),
+        prepare)
+    return call if prepare else (out, lse)
 
 
 def decode(q, k_cache, v_cache, kv_offsets, kv_lens, *, split_len: int, max_splits: int,
