@@ -497,7 +497,6 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     auto iter = [&](int t, auto parity, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
       constexpr int P = decltype(parity)::value;
       if (t + 2 < ntiles) issue_k(t + 2, KST[P]);
-      if (t + 1 < ntiles) issue_v(t + 1, VST[1 - P]);
       const float base = prep(cur, t * BN + kh * KW);
       u32x4 pk[NKS];
       if (t + 1 < ntiles) {
@@ -516,6 +515,9 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
       } else {
         expo(cur, base, pk);
       }
+      // V(t+1) goes out here rather than with K(t+2): its stage held V(t-1),
+      // long consumed, and issuing it mid-tile spreads the DMA over the tile.
+      if (t + 1 < ntiles) issue_v(t + 1, VST[1 - P]);
       pv(lds + VST[P], pk);
       {
         // P.V: V^T operand reads four MFMAs ahead.
