@@ -39,6 +39,19 @@ Causal alignment when Sq < Skv is not stated on the pages. The reading taken
 is bottom-right: query row i sits at absolute position q_pos = i + (Skv - Sq),
 so a single decode query sees every key.
 
+Masks beyond causality ("STAGE_D.md — FMHA Kernel Development", D3: a
+per-sequence length input masks every key index at or past that sequence's
+length; D4: the causal comparison on the same branch). The pages give the two
+as independent conditions; the reading taken is that a key is visible only if
+every enabled condition admits it:
+  * causal:      j <= q_pos;
+  * kv_lens[b]:  j <  kv_lens[b] (a per-sequence valid KV length);
+  * window W>0:  j >  q_pos - W (a sliding window of the W positions up to and
+                 including q_pos; the pages name sliding-window attention but
+                 do not spell out its bound, so this is the plainest reading).
+A row with no visible key has no softmax; the reading taken (as for an empty
+decode split) is O = 0, row_sum = 0, LSE = row_max = -inf.
+
 This is the two-pass form (max first, then exponentials), not an online
 softmax, so it is the definition rather than an algorithm that reaches it.
 """
@@ -76,32 +89,41 @@ def _as_f64(x, dtype: Optional[str]) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                q_pos: Optional[np.ndarray]) -> dict:
+                q_pos: Optional[np.ndarray], visible: Optional[np.ndarray] = None) -> dict:
     """Softmax attention of query rows over keys 0..Skv-1, fp64.
 
     q_rows [R, D]; k, v [Skv, D]; q_pos [R] absolute query positions (causal:
-    key j is visible iff j <= q_pos), or None for no mask.
-    Returns o, lse, row_sum (l), o_unnorm (U), row_max (m), each per row.
+    key j is visible iff j <= q_pos), or None for no causal mask; visible
+    [R, Skv] an optional further boolean mask (True = visible).
+    Returns o, lse, row_sum (l), o_unnorm (U), row_max (m), each per row; a row
+    with no visible key gets o = o_unnorm = 0, row_sum = 0, lse = row_max = -inf.
     """
     scores = (q_rows @ k.T) * float(scale)                       # s_ij
     if q_pos is not None:
         masked = np.arange(k.shape[0])[None, :] > np.asarray(q_pos)[:, None]
         scores = np.where(masked, -np.inf, scores)
+    if visible is not None:
+        scores = np.where(visible, scores, -np.inf)
     m = scores.max(axis=1)                                       # m_i
-    p = np.exp(scores - m[:, None])                              # masked -> exp(-inf) = 0
+    empty = np.isneginf(m)
+    p = np.exp(scores - np.where(empty, 0.0, m)[:, None])        # masked -> exp(-inf) = 0
     l = p.sum(axis=1)                                            # l_i
     u = p @ v                                                    # U_i
-    return {"o": u / l[:, None], "lse": m + np.log(l), "row_sum": l, "o_unnorm": u,
-            "row_max": m}
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.where(empty[:, None], 0.0, u / np.where(empty, 1.0, l)[:, None])
+        lse = np.where(empty, -np.inf, m + np.log(np.where(empty, 1.0, l)))
+    return {"o": o, "lse": lse, "row_sum": l, "o_unnorm": u, "row_max": m}
 
 
 def prefill(q, k, v, *, scale: float, causal: bool = True, dtype: Optional[str] = None,
-            rows: Optional[Iterable[int]] = None) -> dict:
+            rows: Optional[Iterable[int]] = None, kv_lens=None, window: int = 0) -> dict:
     """Attention forward for the whole problem (or for the query rows listed).
 
     q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D]; half bit patterns when ``dtype``
     is given, real numbers otherwise. ``scale`` is the fp32 softmax scale the
-    GPU receives; it is widened to float64 unchanged.
+    GPU receives; it is widened to float64 unchanged. ``kv_lens`` [B] (valid KV
+    length per sequence) and ``window`` (> 0: sliding window) add the masks
+    described in the module docstring.
 
     Returns float64 arrays: o and o_unnorm [B, R, Hq, Dv]; lse, row_sum and
     row_max [B, Hq, R], where R is Sq or len(rows).
@@ -115,14 +137,24 @@ def prefill(q, k, v, *, scale: float, causal: bool = True, dtype: Optional[str] 
     Dv = vf.shape[3]
     rows = np.arange(Sq) if rows is None else np.asarray(list(rows), dtype=np.int64)
     R = rows.shape[0]
-    q_pos = rows + (Skv - Sq) if causal else None
+    pos = rows + (Skv - Sq)                                      # absolute query positions
+    q_pos = pos if causal else None
+    keys = np.arange(Skv)
     out = {"o": np.zeros((B, R, Hq, Dv)), "o_unnorm": np.zeros((B, R, Hq, Dv)),
            "lse": np.zeros((B, Hq, R)), "row_sum": np.zeros((B, Hq, R)),
            "row_max": np.zeros((B, Hq, R))}
     for b in range(B):
+        visible = None
+        if kv_lens is not None or window > 0:
+            visible = np.ones((R, Skv), dtype=bool)
+            if kv_lens is not None:
+                visible &= keys[None, :] < int(kv_lens[b])
+            if window > 0:
+                visible &= keys[None, :] > (pos[:, None] - int(window))
         for h in range(Hq):
             hk = h // group
-            r = attend_rows(qf[b, rows, h, :], kf[b, :, hk, :], vf[b, :, hk, :], scale, q_pos)
+            r = attend_rows(qf[b, rows, h, :], kf[b, :, hk, :], vf[b, :, hk, :], scale, q_pos,
+                            visible)
             out["o"][b, :, h, :] = r["o"]
             out["o_unnorm"][b, :, h, :] = r["o_unnorm"]
             out["lse"][b, h, :] = r["lse"]

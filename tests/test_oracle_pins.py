@@ -455,3 +455,137 @@ def test_generator_sha256_fixed():
     lens = inputs.decode_lengths(inputs.LONG_DECODE, rng)
     assert hashlib.sha256(lens.tobytes()).hexdigest() == want[inputs.LONG_DECODE.name]["kv_lens"]
     assert lens.min() >= 512 and lens.max() <= 32768
+
+
+# --------------------------------------------------------------------------
+# Masks beyond causality: per-sequence KV length and sliding window
+# --------------------------------------------------------------------------
+
+def _mask_inputs(seed, B=2, sq=9, skv=13, hq=4, hkv=2, D=8):
+    rng = np.random.default_rng(seed)
+    return (_rand_half(rng, (B, sq, hq, D)), _rand_half(rng, (B, skv, hkv, D), mult=2.0),
+            _rand_half(rng, (B, skv, hkv, D)))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_masks_that_admit_everything_change_nothing(causal):
+    q, k, v = _mask_inputs(101)
+    scale = float(np.float32(0.3))
+    base = oracle.prefill(q, k, v, scale=scale, causal=causal, dtype="f16")
+    full = oracle.prefill(q, k, v, scale=scale, causal=causal, dtype="f16",
+                          kv_lens=[13, 13], window=13 + 9)
+    for key in ("o", "lse", "row_sum"):
+        assert base[key].tobytes() == full[key].tobytes()
+
+
+def test_kv_length_equals_truncated_cache():
+    """Unmasked attention with kv_lens[b] = L equals attention over the first L keys."""
+    q, k, v = _mask_inputs(102)
+    scale = float(np.float32(0.3))
+    lens = [5, 11]
+    r = oracle.prefill(q, k, v, scale=scale, causal=False, dtype="f16", kv_lens=lens)
+    for b, L in enumerate(lens):
+        t = oracle.prefill(q[b:b + 1], k[b:b + 1, :L], v[b:b + 1, :L], scale=scale, causal=False,
+                           dtype="f16")
+        np.testing.assert_allclose(r["o"][b], t["o"][0], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(r["lse"][b], t["lse"][0], rtol=1e-13, atol=1e-15)
+
+
+def test_window_of_one_is_the_diagonal_key():
+    """Causal window 1: every row sees exactly key q_pos, so O = V[q_pos] exactly and
+    LSE = the exact score."""
+    q, k, v = _mask_inputs(103, B=1, sq=6, skv=9)
+    scale = float(np.float32(0.5))
+    r = oracle.prefill(q, k, v, scale=scale, causal=True, dtype="f16", window=1)
+    off = 9 - 6
+    for i in range(6):
+        for h in range(4):
+            hk = h // 2
+            np.testing.assert_array_equal(r["o"][0, i, h], _f(v[0, i + off, hk]))
+            assert r["lse"][0, h, i] == float(_exact_score(_f(q[0, i, h]), _f(k[0, i + off, hk]),
+                                                           scale))
+
+
+def test_window_equals_sliced_keys():
+    """Causal window W: row i equals unmasked attention over keys q_pos-W+1 .. q_pos."""
+    q, k, v = _mask_inputs(104, B=1, sq=10, skv=10)
+    scale = float(np.float32(0.4))
+    W = 4
+    r = oracle.prefill(q, k, v, scale=scale, causal=True, dtype="f16", window=W)
+    for i in range(10):
+        lo = max(0, i - W + 1)
+        for h in range(4):
+            hk = h // 2
+            t = oracle.attend_rows(_f(q[0, i:i + 1, h]), _f(k[0, lo:i + 1, hk]),
+                                   _f(v[0, lo:i + 1, hk]), scale, None)
+            np.testing.assert_allclose(r["o"][0, i, h], t["o"][0], rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(r["lse"][0, h, i], t["lse"][0], rtol=1e-13, atol=1e-15)
+
+
+def test_masked_keys_do_not_matter_bitwise():
+    """Changing K/V rows outside every row's window and past each sequence's length
+    leaves all outputs bit-identical."""
+    q, k, v = _mask_inputs(105, B=2, sq=8, skv=12)
+    scale = float(np.float32(0.3))
+    lens, W = [9, 12], 3
+    r = oracle.prefill(q, k, v, scale=scale, causal=True, dtype="f16", kv_lens=lens, window=W)
+    k2, v2 = k.copy(), v.copy()
+    rng = np.random.default_rng(7)
+    # rows are at positions 4..11: keys 0 and 1 are below every window; keys >= len are cut
+    for b, L in enumerate(lens):
+        for j in list(range(0, 2)) + list(range(L, 12)):
+            k2[b, j] = _rand_half(rng, k2[b, j].shape, mult=4.0)
+            v2[b, j] = _rand_half(rng, v2[b, j].shape, mult=4.0)
+    r2 = oracle.prefill(q, k2, v2, scale=scale, causal=True, dtype="f16", kv_lens=lens, window=W)
+    for key in ("o", "lse", "row_sum"):
+        assert r[key].tobytes() == r2[key].tobytes()
+
+
+def test_rows_without_visible_keys():
+    """A window that ends before the sequence's valid length starts leaves a row
+    without keys: O = 0, row_sum = 0, LSE = -inf; the other rows are unaffected."""
+    q, k, v = _mask_inputs(106, B=1, sq=8, skv=8)
+    scale = float(np.float32(0.3))
+    r = oracle.prefill(q, k, v, scale=scale, causal=True, dtype="f16", kv_lens=[3], window=2)
+    # row i (q_pos = i) sees keys max(0, i-1) .. min(i, 2): empty from i = 4 on
+    for i in range(8):
+        if i >= 4:
+            assert np.all(r["o"][0, i] == 0) and np.all(np.isneginf(r["lse"][0, :, i]))
+            assert np.all(r["row_sum"][0, :, i] == 0)
+        else:
+            assert np.all(np.isfinite(r["lse"][0, :, i]))
+
+
+def _decimal_masked(qf, kf, vf, scale, visible):
+    getcontext().prec = 60
+    sc = Decimal(scale)
+    sq = qf.shape[0]
+    out_o = np.zeros((sq, vf.shape[1]))
+    out_lse = np.full(sq, -np.inf)
+    for i in range(sq):
+        js = [j for j in range(kf.shape[0]) if visible(i, j)]
+        if not js:
+            continue
+        ex = [(sum(Decimal(float(qf[i, d])) * Decimal(float(kf[j, d]))
+                   for d in range(qf.shape[1])) * sc).exp() for j in js]
+        tot = sum(ex)
+        out_lse[i] = float(tot.ln())
+        for d in range(vf.shape[1]):
+            out_o[i, d] = float(sum(e * Decimal(float(vf[j, d])) for j, e in zip(js, ex)) / tot)
+    return out_o, out_lse
+
+
+@pytest.mark.parametrize("causal,L,W", [(True, 5, 3), (False, 6, 2), (True, 7, 0)])
+def test_brute_force_decimal_masks(causal, L, W):
+    sq, skv, D = 5, 7, 3
+    q, k, v = _mask_inputs(107 + L + W, B=1, sq=sq, skv=skv, hq=2, hkv=1, D=D)
+    scale = float(np.float32(0.7))
+    r = oracle.prefill(q, k, v, scale=scale, causal=causal, dtype="f16", kv_lens=[L], window=W)
+
+    def visible(i, j):
+        pos = i + skv - sq
+        return (j <= pos or not causal) and j < L and (W == 0 or j > pos - W)
+    for h in range(2):
+        o, lse = _decimal_masked(_f(q[0, :, h]), _f(k[0, :, 0]), _f(v[0, :, 0]), scale, visible)
+        np.testing.assert_allclose(r["o"][0, :, h], o, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(r["lse"][0, h], lse, rtol=1e-13, atol=1e-14)
