@@ -80,6 +80,14 @@ int check_attn(const char* fn, const void* q, int64_t q_sb, int64_t q_ss, int64_
   return FA_OK;
 }
 
+// Length mask and sliding window of a prefill call.
+int check_masks(const char* fn, const int32_t* kv_lens, int window) {
+  if (window < 0) return fail(FA_ERR_INVALID_ARG, "%s: window (%d) must be >= 0", fn, window);
+  if (kv_lens && ((uintptr_t)kv_lens & 3u))
+    return fail(FA_ERR_INVALID_ARG, "%s: kv_lens must be 4-byte aligned", fn);
+  return FA_OK;
+}
+
 // Value side of a prefill call (the tensor repacked into the workspace).
 int check_pack(const char* fn, const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh) {
   if (!v) return fail(FA_ERR_INVALID_ARG, "%s: q, k, v, o and lse must be non-null", fn);
@@ -106,7 +114,8 @@ fa::PrefillArgs prefill_args(const void* q, int64_t q_sb, int64_t q_ss, int64_t 
                              const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh, float* o,
                              int64_t o_sb, int64_t o_ss, int64_t o_sh, float* lse,
                              float* row_sum, int batch, int seqlen_q, int seqlen_kv,
-                             int n_heads_q, int n_heads_kv, int causal, float softmax_scale) {
+                             int n_heads_q, int n_heads_kv, int causal, float softmax_scale,
+                             const int32_t* kv_lens, int window) {
   fa::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_sum = row_sum;
   a.q_sb = q_sb; a.q_ss = q_ss; a.q_sh = q_sh;
@@ -117,6 +126,8 @@ fa::PrefillArgs prefill_args(const void* q, int64_t q_sb, int64_t q_ss, int64_t 
   a.n_heads_q = n_heads_q; a.n_heads_kv = n_heads_kv;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = softmax_scale * kLog2e;
+  a.kv_lens = kv_lens;
+  a.window = window;
   return a;
 }
 
@@ -143,12 +154,13 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                    float* lse, float* row_sum,
                    int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                    int head_dim, int dtype, int causal, float softmax_scale,
-                   int out_unnormalized, void* workspace, uint64_t workspace_bytes,
-                   void* stream) {
+                   int out_unnormalized, const int32_t* kv_lens, int window,
+                   void* workspace, uint64_t workspace_bytes, void* stream) {
   const char* fn = "fa_prefill_fwd";
   int st = check_attn(fn, q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, o, o_sb, o_ss, o_sh, lse,
                       row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, dtype,
                       softmax_scale, out_unnormalized);
+  if (st == FA_OK) st = check_masks(fn, kv_lens, window);
   if (st == FA_OK) st = check_pack(fn, v, v_sb, v_ss, v_sh);
   if (st == FA_OK)
     st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
@@ -156,7 +168,7 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
   const fa::PrefillArgs a =
       prefill_args(q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, v, v_sb, v_ss, v_sh, o, o_sb, o_ss,
                    o_sh, lse, row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, causal,
-                   softmax_scale);
+                   softmax_scale, kv_lens, window);
   const fa::VtArgs w{workspace, (size_t)workspace_bytes};
   const hipError_t e =
       fa::launch_prefill_pack(a, w, head_dim, dtype == FA_BF16, (hipStream_t)stream);
@@ -194,19 +206,20 @@ int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_s
                           float* lse, float* row_sum,
                           int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                           int head_dim, int dtype, int causal, float softmax_scale,
-                          int out_unnormalized, const void* workspace, uint64_t workspace_bytes,
-                          void* stream) {
+                          int out_unnormalized, const int32_t* kv_lens, int window,
+                          const void* workspace, uint64_t workspace_bytes, void* stream) {
   const char* fn = "fa_prefill_fwd_packed";
   int st = check_attn(fn, q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, o, o_sb, o_ss, o_sh, lse,
                       row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, dtype,
                       softmax_scale, out_unnormalized);
+  if (st == FA_OK) st = check_masks(fn, kv_lens, window);
   if (st == FA_OK)
     st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
   if (st != FA_OK) return st;
   const fa::PrefillArgs a =
       prefill_args(q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, nullptr, 0, 0, 0, o, o_sb, o_ss,
                    o_sh, lse, row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, causal,
-                   softmax_scale);
+                   softmax_scale, kv_lens, window);
   const fa::VtArgs w{const_cast<void*>(workspace), (size_t)workspace_bytes};
   return hip_status(fa::launch_prefill_attn(a, w, head_dim, dtype == FA_BF16,
                                             out_unnormalized != 0, (hipStream_t)stream),

@@ -20,7 +20,9 @@ struct PrefillArgs {
   int64_t o_sb, o_ss, o_sh;
   int batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv;
   int causal;
-  float scale_log2;  // softmax_scale * log2(e)
+  float scale_log2;        // softmax_scale * log2(e)
+  const int32_t* kv_lens;  // device [batch] valid KV length per sequence, or null
+  int window;              // > 0: key j visible only if j > q_pos - window
 };
 
 struct DecodeArgs {

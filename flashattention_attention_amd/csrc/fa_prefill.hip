@@ -340,9 +340,16 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   };
 
   // KV range: keys up to the largest query position of the block.
-  int kv_end = a.seqlen_kv;
-  if (a.causal) kv_end = min(a.seqlen_kv, min(q0 + kBM, a.seqlen_q) + off);
-  const int ntiles = (kv_end + BN - 1) / BN;
+  // Keys this work-group may see: [kv_lo, kv_end). The causal bound and the
+  // sequence's valid length cap the end; a sliding window raises the start
+  // (for the block's first row). Tiles wholly outside are never touched; the
+  // loop below runs over tiles tb .. tb + ntiles - 1.
+  const int kv_len = a.kv_lens ? min(max(a.kv_lens[b], 0), a.seqlen_kv) : a.seqlen_kv;
+  int kv_end = kv_len;
+  if (a.causal) kv_end = min(kv_end, min(q0 + kBM, a.seqlen_q) + off);
+  const int kv_lo = a.window > 0 ? max(0, q0 + off - a.window + 1) : 0;
+  const int tb = kv_lo / BN;
+  const int ntiles = kv_end > kv_lo ? (kv_end + BN - 1) / BN - tb : 0;
   const int ntiles_all = (a.seqlen_kv + BN - 1) / BN;
   const int wave_first_qpos = q0 + qw * 32 + off;
 
@@ -361,9 +368,10 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   }
   const unsigned lds_base = (unsigned)(uintptr_t)(lptr_t)lds;
 
-  // DMA of this wave's share of the K rows / V^T bytes of tile t to LDS offset dst.
+  // DMA of this wave's share of the K rows / V^T bytes of tile tb + t to LDS
+  // offset dst.
   auto issue_k = [&](int t, unsigned dst) {
-    const int t0 = t * BN;
+    const int t0 = (tb + t) * BN;
     const bool full = t0 + BN <= a.seqlen_kv;
 #pragma unroll
     for (int j = 0; j < K_INSTR; ++j) {
@@ -382,7 +390,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
 #pragma unroll
     for (int j = 0; j < V_INSTR; ++j) {
       const int J = wave * V_INSTR + j;
-      dma16(vtp + (int64_t)t * VT + J * 1024 + lane * 16, lds_base + dst + J * 1024);
+      dma16(vtp + (int64_t)(tb + t) * VT + J * 1024 + lane * 16, lds_base + dst + J * 1024);
     }
   };
 
@@ -421,15 +429,19 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   // Mask, row max and (rarely) the move of the exponent base; returns the base.
   // Element i of block kb holds key t0 + kb*32 + (i/4)*8 + hh*4 + i%4.
   auto prep = [&](f32x16 (&s)[NKB], int t0) -> float {
-    const bool need_mask =
-        (a.causal && t0 + KW - 1 > wave_first_qpos) || (t0 + KW > a.seqlen_kv);
+    const bool need_mask = (a.causal && t0 + KW - 1 > wave_first_qpos) || (t0 + KW > kv_len) ||
+                           (a.window > 0 && t0 <= wave_first_qpos + 31 - a.window);
     if (need_mask) {
-      const int lim = min(a.causal ? qpos : INT_MAX, a.seqlen_kv - 1) - t0 - hh * 4;
+      // visible: lo <= key offset <= hi, offsets relative to t0 + hh*4
+      const int hi = min(a.causal ? qpos : INT_MAX, kv_len - 1) - t0 - hh * 4;
+      const int lo = a.window > 0 ? qpos - a.window + 1 - t0 - hh * 4 : INT_MIN;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kb][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int j = kb * 32 + (i >> 2) * 8 + (i & 3);
+          if (j > hi || j < lo) s[kb][i] = -INFINITY;
+        }
     }
     float mx = s[0][0];
 #pragma unroll
@@ -497,7 +509,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     auto iter = [&](int t, auto parity, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
       constexpr int P = decltype(parity)::value;
       if (t + 2 < ntiles) issue_k(t + 2, KST[P]);
-      const float base = prep(cur, t * BN + kh * KW);
+      const float base = prep(cur, (tb + t) * BN + kh * KW);
       u32x4 pk[NKS];
       if (t + 1 < ntiles) {
         qk(lds + KST[1 - P], nxt);
@@ -545,7 +557,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
       if (t + 1 < ntiles) { issue_k(t + 1, ST_[1 - ST]); issue_v(t + 1, ST_[1 - ST] + KT); }
       f32x16 sc[NKB];
       qk(lds + ST_[ST], sc);
-      const float base = prep(sc, t * BN + kh * KW);
+      const float base = prep(sc, (tb + t) * BN + kh * KW);
       u32x4 pk[NKS];
       expo(sc, base, pk);
       pv(lds + ST_[ST] + KT, pk);
@@ -602,7 +614,8 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
 
   // Refer the outputs back to the true row max: factor = 2^((m_used - kShift) - m_true).
   const float to_true = exp2_fast(m_used - kShift - m_true);
-  const float f = UNNORM ? to_true : 1.0f / lt;
+  // a row with no visible key (length or window mask) has lt = 0: O = 0, LSE = -inf
+  const float f = UNNORM ? to_true : (lt > 0.0f ? 1.0f / lt : 0.0f);
   if (hh == 0 && q_valid) {
     const int64_t ri = ((int64_t)b * a.n_heads_q + h) * a.seqlen_q + qi;
     a.lse[ri] = (m_used - kShift + __log2f(lt)) * kLn2;

@@ -29,13 +29,13 @@ _SIGNATURES = {
     "fa_prefill_fwd": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                         _vp, _i64, _i64, _i64, _vp, _vp,
                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
-                        _vp, ctypes.c_uint64, _vp], _i32),
+                        _vp, _i32, _vp, ctypes.c_uint64, _vp], _i32),
     "fa_prefill_pack_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                            _vp, ctypes.c_uint64, _vp], _i32),
     "fa_prefill_fwd_packed": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                _vp, _i64, _i64, _i64, _vp, _vp,
                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
-                               _vp, ctypes.c_uint64, _vp], _i32),
+                               _vp, _i32, _vp, ctypes.c_uint64, _vp], _i32),
     "fa_prefill_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
     "fa_decode_plan": ([ctypes.POINTER(ctypes.c_int32), _i32, _i32, _i32, _i32, _i32,
                         ctypes.POINTER(_i32), ctypes.POINTER(_i32)], _i32),
@@ -163,6 +163,21 @@ def _prefill_outputs(q, k, dev, out, lse, row_sum, out_unnormalized, want_row_su
     return out, lse, row_sum, need_rs
 
 
+def _masks(kv_lens, window, batch, dev):
+    """Marshal the optional length mask (int32 GPU tensor [batch]) and window."""
+    window = int(window)
+    if window < 0:
+        raise FAError("window must be >= 0")
+    if kv_lens is None:
+        return None, window
+    _on_gpu(kv_lens)
+    if kv_lens.device != dev:
+        raise FAError("kv_lens must be on the same GPU as q")
+    if kv_lens.dtype != torch.int32 or kv_lens.shape != (batch,) or not kv_lens.is_contiguous():
+        raise FAError("kv_lens must be a contiguous int32 tensor [batch]")
+    return kv_lens, window
+
+
 def _workspace(k, dev, workspace):
     B, Skv, Hkv, D = k.shape
     ws_need = load_library().fa_prefill_workspace_size(B, Skv, Hkv, D)
@@ -178,8 +193,14 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
             softmax_scale: Optional[float] = None, out_unnormalized: bool = False,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
             row_sum: Optional[torch.Tensor] = None, want_row_sum: bool = False,
-            workspace: Optional[torch.Tensor] = None):
+            workspace: Optional[torch.Tensor] = None, kv_lens: Optional[torch.Tensor] = None,
+            window: int = 0):
     """Attention forward. q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (fp16/bf16, D contiguous).
+
+    ``kv_lens`` (optional int32 GPU tensor [B]) hides keys j >= kv_lens[b];
+    ``window`` > 0 hides keys j <= p - window for the query at position p
+    (p = row + Skv - Sq). Rows that see no key come back with o = 0,
+    lse = -inf.
 
     ``workspace`` (optional) is a uint8 GPU tensor of at least
     ``prefill_workspace_size(...)`` bytes; one is allocated when omitted.
@@ -198,6 +219,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
+    kv_lens, window = _masks(kv_lens, window, B, dev)
     workspace = _workspace(k, dev, workspace)
     st = load_library().fa_prefill_fwd(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
@@ -206,8 +228,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
         B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
-        1 if out_unnormalized else 0, workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(dev))
+        1 if out_unnormalized else 0, kv_lens.data_ptr() if kv_lens is not None else None,
+        window, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(dev))
     _check(st, "fa_prefill_fwd")
     return (out, lse, row_sum) if need_rs else (out, lse)
 
@@ -232,7 +255,8 @@ def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
                    causal: bool = True, softmax_scale: Optional[float] = None,
                    out_unnormalized: bool = False, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, row_sum: Optional[torch.Tensor] = None,
-                   want_row_sum: bool = False, prepare: bool = False):
+                   want_row_sum: bool = False, kv_lens: Optional[torch.Tensor] = None,
+                   window: int = 0, prepare: bool = False):
     """prefill() with V taken from a workspace filled by prefill_pack_v (same shapes).
     With prepare=True, returns a callable that repeats the call (pass the outputs)."""
     dev = _on_gpu(q, k, packed_v)
@@ -241,15 +265,16 @@ def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
+    kv_lens, window = _masks(kv_lens, window, B, dev)
     call = _issue("fa_prefill_fwd_packed", (
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
         B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
-        1 if out_unnormalized else 0, packed_v.data_ptr(),
-        packed_v.numel() * packed_v.element_size(), _stream(dev)),
-        (q, k, packed_v, out, lse, row_sum), prepare)
+        1 if out_unnormalized else 0, kv_lens.data_ptr() if kv_lens is not None else None,
+        window, packed_v.data_ptr(), packed_v.numel() * packed_v.element_size(), _stream(dev)),
+        (q, k, packed_v, out, lse, row_sum, kv_lens), prepare)
     if prepare:
         return call
     return (out, lse, row_sum) if need_rs else (out, lse)

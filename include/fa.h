@@ -57,7 +57,8 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  * fa_prefill_fwd — attention forward over a whole prompt.
  *
  * Source: "STAGE_D.md — FMHA Kernel Development", "Kernel Output" (O, row
- * sum, LSE; external normalization) and D3/D4 (mask comparator); "60 · r57 —
+ * sum, LSE; external normalization), D3 (per-sequence length mask) and D4
+ * (causal mask on the windowed branch); "60 · r57 —
  * FA KV staging double buffering (REVERTED)", sections 1 and 2.2 (grid over
  * query block and head, KV tiles streamed up to the causal bound).
  *
@@ -69,9 +70,21 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  *   lse     [batch, n_heads_q, seqlen_q] fp32, contiguous (natural-log LSE)
  *   row_sum [batch, n_heads_q, seqlen_q] fp32, contiguous, or NULL
  *
- * causal != 0: query row i sits at position i + (seqlen_kv - seqlen_q)
- * (bottom-right alignment) and sees keys j <= that position. causal == 0:
- * every key is visible.
+ * Query row i sits at position p_i = i + (seqlen_kv - seqlen_q) (bottom-right
+ * alignment). Key j is visible to row i when every enabled mask admits it:
+ *   causal != 0       j <= p_i                (D4: causal mask)
+ *   kv_lens != NULL   j < kv_lens[b]          (D3: per-sequence length mask)
+ *   window > 0        j > p_i - window        (sliding window of `window`
+ *                                              positions ending at p_i)
+ * kv_lens is a DEVICE array [batch] of int32 (4-byte aligned) or NULL (all
+ * seqlen_kv keys valid); each value is clamped to [0, seqlen_kv] on the
+ * device. window == 0 disables the window; window < 0 is rejected. The masks
+ * combine freely (causal == 0 with a window admits every key after
+ * p_i - window). A row that sees no key gets o = 0, row_sum = 0 and
+ * lse = -inf. Hidden keys that share a 64-key tile with visible ones are read
+ * and given weight zero, so K and V must hold finite values there too (V
+ * within fp16 range; padding past kv_lens[b] included); tiles with no visible
+ * key are skipped.
  *
  * out_unnormalized == 0: o = normalized output; row_sum (optional) = l_i.
  * out_unnormalized != 0: o = sum_j P_ij v[j,:] with P_ij = exp(s_ij - m_i)
@@ -100,8 +113,8 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                    float* lse, float* row_sum,
                    int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                    int head_dim, int dtype, int causal, float softmax_scale,
-                   int out_unnormalized, void* workspace, uint64_t workspace_bytes,
-                   void* stream);
+                   int out_unnormalized, const int32_t* kv_lens, int window,
+                   void* workspace, uint64_t workspace_bytes, void* stream);
 
 /*
  * fa_prefill_pack_v / fa_prefill_fwd_packed — fa_prefill_fwd in its two
@@ -133,8 +146,8 @@ int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_s
                           float* lse, float* row_sum,
                           int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                           int head_dim, int dtype, int causal, float softmax_scale,
-                          int out_unnormalized, const void* workspace, uint64_t workspace_bytes,
-                          void* stream);
+                          int out_unnormalized, const int32_t* kv_lens, int window,
+                          const void* workspace, uint64_t workspace_bytes, void* stream);
 
 /*
  * fa_prefill_workspace_size — bytes of workspace fa_prefill_fwd needs

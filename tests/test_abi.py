@@ -83,14 +83,15 @@ def _prefill(**kw):
     base = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED, row_sum=None,
                 B=1, Sq=128, Skv=128, Hq=4, Hkv=2, D=128, dtype=0, causal=1, scale=0.125,
                 unnorm=0, qs=(128 * 4 * 128, 4 * 128, 128), ks=(128 * 2 * 128, 2 * 128, 128),
-                os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40)
+                os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40, lens=None, win=0)
     base.update(kw)
     b = base
     lib = fa.load_library()
     return lib.fa_prefill_fwd(b["q"], *b["qs"], b["k"], *b["ks"], b["v"], *b["ks"],
                               b["o"], *b["os"], b["lse"], b["row_sum"], b["B"], b["Sq"],
                               b["Skv"], b["Hq"], b["Hkv"], b["D"], b["dtype"], b["causal"],
-                              b["scale"], b["unnorm"], b["ws"], b["wsb"], None)
+                              b["scale"], b["unnorm"], b["lens"], b["win"], b["ws"], b["wsb"],
+                              None)
 
 
 @pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
@@ -103,6 +104,7 @@ def _prefill(**kw):
     (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1), (dict(os=(128, 2, 128)), 1),
     (dict(ks=(-8, 256, 128)), 1), (dict(Sq=2**31 - 1, Skv=2**31 - 1, Hq=128), 2),
     (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(ws=ALIGNED + 16), 1),
+    (dict(win=-1), 1), (dict(lens=ALIGNED + 2), 1),
 ])
 def test_prefill_validation(kw, status):
     st = _prefill(**kw)
@@ -131,18 +133,19 @@ def test_prefill_pack_v_validation(kw, status):
     (dict(q=None), 1), (dict(k=None), 1), (dict(lse=None), 1), (dict(unnorm=1), 1),
     (dict(Skv=64), 1), (dict(Hkv=3), 1), (dict(D=512), 2), (dict(scale=0.0), 1),
     (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1),
+    (dict(win=-3), 1), (dict(lens=ALIGNED + 1), 1),
 ])
 def test_prefill_fwd_packed_validation(kw, status):
     b = dict(q=ALIGNED, k=ALIGNED, o=ALIGNED, lse=ALIGNED, row_sum=None, B=1, Sq=128, Skv=128,
              Hq=4, Hkv=2, D=128, dtype=0, causal=1, scale=0.125, unnorm=0,
              qs=(128 * 4 * 128, 4 * 128, 128), ks=(128 * 2 * 128, 2 * 128, 128),
-             os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40)
+             os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40, lens=None, win=0)
     b.update(kw)
     lib = fa.load_library()
     st = lib.fa_prefill_fwd_packed(b["q"], *b["qs"], b["k"], *b["ks"], b["o"], *b["os"],
                                    b["lse"], b["row_sum"], b["B"], b["Sq"], b["Skv"], b["Hq"],
                                    b["Hkv"], b["D"], b["dtype"], b["causal"], b["scale"],
-                                   b["unnorm"], b["ws"], b["wsb"], None)
+                                   b["unnorm"], b["lens"], b["win"], b["ws"], b["wsb"], None)
     assert st == status, lib.fa_last_error()
 
 
