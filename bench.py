@@ -8,11 +8,12 @@ HBM before the timed region.
 
 Prints one JSON line. ``value`` is the prefill's algorithmic throughput in
 TFLOP/s (4 * head_dim FLOPs per visible query/key pair, per query head) over
-both of its launches (V repack + attention), timed with HIP events on the
-launch stream; the roofline entry uses the attention launch alone. The same line carries the
+both of its launches (V repack + attention), timed with HIP events (without
+system fence) on the launch stream; the roofline entry uses the attention
+launch alone. The same line carries the
 decode timings, the batched long-context decode (32 sequences, 512..32768
-tokens) and the large-head prefill (head_dim 256, 8192 tokens) as extra
-measurements, a roofline entry per kernel family, and the fp64 CPU oracle's
+tokens), the large-head prefill (head_dim 256, 8192 tokens) and the GQA prompt
+under a 1024-position sliding window as extra measurements, a roofline entry per kernel family, and the fp64 CPU oracle's
 throughput on a bounded sample of the prefill workload.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
@@ -40,8 +41,57 @@ def _dev(torch, bits, dtype):
     return t.view(torch.float16 if dtype == "f16" else torch.bfloat16).cuda()
 
 
+class _HipEvent:
+    """A HIP timing event recorded on the current stream without the
+    system-scope release fence that a default event adds (that fence costs a
+    few microseconds per record and would be timed as part of the kernels
+    around it). The launches are ordered on the stream, so each timestamp is
+    taken after the preceding kernel has completed."""
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            lib = ctypes.CDLL("libamdhip64.so.7")      # the runtime torch has loaded
+            vp = ctypes.c_void_p
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [vp, vp]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            lib.hipEventDestroy.argtypes = [vp]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self, torch):
+        import ctypes
+        self._torch = torch
+        self._ev = ctypes.c_void_p()
+        st = self._lib().hipEventCreateWithFlags(ctypes.byref(self._ev),
+                                                 0x20000000)   # hipEventDisableSystemFence
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {st}")
+
+    def record(self):
+        st = self._lib().hipEventRecord(self._ev, self._torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed: {st}")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        st = self._lib().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {st}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._ev:
+            self._hip.hipEventDestroy(self._ev)
+
+
 def _events(torch, n):
-    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    return [_HipEvent(torch) for _ in range(n)]
 
 
 def prefill_setup(torch, fa, cfg):
@@ -61,7 +111,7 @@ def prefill_setup(torch, fa, cfg):
     pack = fa.prefill_pack_v(v, workspace=ws, prepare=True)
     attn = fa.prefill_packed(q, k, ws, causal=cfg.causal, softmax_scale=cfg.scale,
                              out_unnormalized=cfg.out_unnormalized, out=o, lse=lse, row_sum=rs,
-                             prepare=True)
+                             window=cfg.window, prepare=True)
 
     def run():
         pack()
@@ -201,8 +251,9 @@ def run_profiling_aid(torch, fa, inputs, args):
         dst = torch.empty_like(src)
         fns = [lambda: dst.copy_(src)]
         label = f"copy {args.copy_bytes} bytes"
-    elif args.only in ("prefill", "large_head"):
-        cfg = inputs.GQA_PREFILL if args.only == "prefill" else inputs.LARGE_HEAD
+    elif args.only in ("prefill", "large_head", "window"):
+        cfg = {"prefill": inputs.GQA_PREFILL, "large_head": inputs.LARGE_HEAD,
+               "window": inputs.WINDOW_PREFILL}[args.only]
         _, pack, attn = prefill_setup(torch, fa, cfg)
         fns, label = [pack, attn], cfg.name
     else:
@@ -222,12 +273,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200)   # ~30 ms: lets the clocks settle
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--split-sweep", action="store_true",
                     help="also time the single-token decode at several split lengths")
-    ap.add_argument("--only", choices=["prefill", "decode", "long_decode", "large_head"],
+    ap.add_argument("--only", choices=["prefill", "decode", "long_decode", "large_head",
+                                              "window"],
                     help="profiling aid: run only this component (warmup + steps) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="profiling aid: time a plain device-to-device copy of this many "
@@ -411,6 +463,30 @@ def main():
             "traffic": measured_traffic(hk, hcfg.name, "fa_prefill.hip"), "kernel": hk,
             "us_per_launch": round(r[1]["mean_ms"] * 1e3, 1),
             "per_launch": f"{hf / 1e12:.4f} TFLOP"}
+        del h_run, h_pack, h_attn
+        print("[bench] windowed prefill", file=sys.stderr, flush=True)
+
+        wcfg = inputs.WINDOW_PREFILL
+        w_run, w_pack, w_attn = prefill_setup(torch, fa, wcfg)
+        w_run()
+        r = time_calls(torch, [w_pack, w_attn], 20)
+        wf = wcfg.flops()
+        w_ms = r[0]["mean_ms"] + r[1]["mean_ms"]
+        wa = wf / (r[1]["mean_ms"] * 1e-3) / 1e12
+        line["prefill_window"] = {"workload": wcfg.name, "window": wcfg.window,
+                                  "us_per_call": round(w_ms * 1e3, 1),
+                                  "attention_us": round(r[1]["mean_ms"] * 1e3, 1),
+                                  "tflops": round(wf / (w_ms * 1e-3) / 1e12, 2),
+                                  "frac_mfma_peak": round(wf / (w_ms * 1e-3) / 1e12
+                                                          / MI355X_BF16_DENSE_TFLOPS, 4)}
+        wk = prefill_kernel_name(wcfg)
+        rooflines["prefill_window1024"] = {
+            "bound": "mfma", "achieved": round(wa, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(wa / MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": measured_traffic(wk, wcfg.name, "fa_prefill.hip"), "kernel": wk,
+            "us_per_launch": round(r[1]["mean_ms"] * 1e3, 1),
+            "per_launch": f"{wf / 1e12:.4f} TFLOP (visible pairs only)"}
+        del w_run, w_pack, w_attn
         del flush_buf
 
     line["roofline"] = rooflines["prefill_gqa_s3314"]

@@ -93,6 +93,7 @@ class PrefillConfig:
     seed: int
     k_mult: float = 1.0
     out_unnormalized: bool = False
+    window: int = 0                        # > 0: sliding window over key positions
 
     @property
     def scale(self) -> float:
@@ -102,10 +103,13 @@ class PrefillConfig:
     def visible_pairs(self) -> int:
         """Number of (query, key) pairs the mask leaves visible, per (batch, head)."""
         sq, skv = self.seqlen_q, self.seqlen_kv
-        if not self.causal:
-            return sq * skv
-        off = skv - sq  # bottom-right alignment: row i sees keys 0 .. i + off
-        return sum(i + off + 1 for i in range(sq))
+        off = skv - sq  # bottom-right alignment: row i sits at position i + off
+        total = 0
+        for i in range(sq):
+            hi = i + off if self.causal else skv - 1
+            lo = max(0, i + off - self.window + 1) if self.window > 0 else 0
+            total += max(0, hi - lo + 1)
+        return total
 
     def flops(self) -> int:
         """Algorithmic FLOPs: 2*D for Q.K^T plus 2*D for P.V per visible pair."""
@@ -141,8 +145,13 @@ LONG_DECODE = DecodeConfig("batched_long_decode_b32_h32kv8_d128_kv512to32768_f16
 LARGE_HEAD = PrefillConfig("large_head_causal_prefill_b2_h16_d256_s8192_bf16_unnorm", 2, 16, 16,
                            256, 8192, 8192, "bf16", True, seed=5, k_mult=4.0,
                            out_unnormalized=True)
+# The GQA prompt under a 1024-position sliding window: about 3/5 of the causal
+# pairs, with whole key tiles skipped on the left of every query block.
+WINDOW_PREFILL = PrefillConfig("gqa_window1024_causal_prefill_b1_h28kv4_d128_s3314_bf16", 1, 28,
+                               4, 128, 3314, 3314, "bf16", True, seed=6, window=1024)
 
-WORKLOADS = {c.name: c for c in (TINY_CAUSAL, GQA_PREFILL, GQA_DECODE, LONG_DECODE, LARGE_HEAD)}
+WORKLOADS = {c.name: c for c in (TINY_CAUSAL, GQA_PREFILL, GQA_DECODE, LONG_DECODE, LARGE_HEAD,
+                                 WINDOW_PREFILL)}
 
 
 def make_prefill_inputs(cfg: PrefillConfig, seed: Optional[int] = None) -> dict:
