@@ -177,6 +177,10 @@ def decode_setup(torch, fa, cfg, split_len=None):
                                       max_splits=max_splits, softmax_scale=cfg.scale,
                                       part_o=po, part_lse=pl, prepare=True)
     merge = fa.decode_merge_lse(po, pl, lens, split_len=split_len, out=o, lse=lse, prepare=True)
+    ws = torch.zeros(fa.decode_fused_workspace_size(B, Hq, cfg.n_heads_kv, D, max_splits),
+                     dtype=torch.uint8, device="cuda")
+    fused = fa.decode_fused(q, kc, vc, offs, lens, split_len=split_len, max_splits=max_splits,
+                            softmax_scale=cfg.scale, out=o, lse=lse, workspace=ws, prepare=True)
 
     kv_bytes = inputs.decode_kv_bytes(x["kv_lens"], cfg.n_heads_kv, cfg.head_dim)
     alg_bytes = kv_bytes + q.numel() * 2 + o.numel() * 4 + lse.numel() * 4
@@ -184,7 +188,7 @@ def decode_setup(torch, fa, cfg, split_len=None):
     part_bytes = 2 * n_parts * (D + 1) * 4           # written once, read once
     return partial, merge, {"split_len": split_len, "max_splits": max_splits,
                             "kv_bytes": kv_bytes, "alg_bytes": alg_bytes,
-                            "partial_bytes": part_bytes}
+                            "partial_bytes": part_bytes, "fused": fused}
 
 
 def time_calls(torch, fns, iters, flush=None):
@@ -396,6 +400,11 @@ def main():
         line["decode_gqa_kv1641"]["cold_us"] = round(
             (cold[0]["median_ms"] + cold[1]["median_ms"]) * 1e3, 2)
         line["decode_gqa_kv1641"]["hot_us"] = round(hot_ms * 1e3, 2)
+        fc = time_calls(torch, [dinfo["fused"]], 20, flush=flush)
+        fh = time_calls(torch, [dinfo["fused"]], 50)
+        line["decode_gqa_kv1641"]["fused_single_launch"] = {
+            "cold_us": round(fc[0]["median_ms"] * 1e3, 2),
+            "hot_us": round(fh[0]["mean_ms"] * 1e3, 2)}
         if args.split_sweep:
             sweep = {}
             for sl in (16, 32, 48, 64, 112, 208):
@@ -419,6 +428,8 @@ def main():
             l_partial(); l_merge()
         r = time_calls(torch, [l_partial, l_merge], 20, flush=flush)
         tot_ms = r[0]["median_ms"] + r[1]["median_ms"]
+        rf = time_calls(torch, [linfo["fused"]], 20, flush=flush)
+        fused_ms = rf[0]["median_ms"]
         part_gbps = (linfo["kv_bytes"] + 0.0) / (r[0]["median_ms"] * 1e-3) / 1e9
         line["decode_batched_long"] = {
             "workload": lcfg.name, "split_len": linfo["split_len"],
@@ -430,6 +441,9 @@ def main():
             "frac_hbm_peak": round(linfo["alg_bytes"] / (tot_ms * 1e-3) / 1e9 / MI355X_HBM_GBPS,
                                    4),
             "partial_bytes_overhead_gb": round(linfo["partial_bytes"] / 1e9, 4),
+            "fused_single_launch_us": round(fused_ms * 1e3, 1),
+            "fused_frac_hbm_peak": round(linfo["alg_bytes"] / (fused_ms * 1e-3) / 1e9
+                                         / MI355X_HBM_GBPS, 4),
             "cache": "flushed (512 MB write) before every call"}
         dk = decode_kernel_name(lcfg)
         rooflines["decode_partial_batched_long"] = {
@@ -439,7 +453,7 @@ def main():
             "us_per_launch": round(r[0]["median_ms"] * 1e3, 1),
             "per_launch": f"{linfo['kv_bytes'] / 1e9:.4f} GB of K+V (each cached key and value "
                           f"row read once)"}
-        del l_partial, l_merge
+        del l_partial, l_merge, linfo
         torch.cuda.empty_cache()
         print("[bench] large-head prefill", file=sys.stderr, flush=True)
 

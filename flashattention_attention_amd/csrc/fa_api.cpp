@@ -289,6 +289,57 @@ int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Query/cache side of a decode call (shared by the split and fused forms).
+int check_decode(const char* fn, const void* q, int64_t q_sb, int64_t q_sh, const void* k_cache,
+                 const void* v_cache, int64_t kv_stride_tok, int64_t kv_stride_head,
+                 const int64_t* kv_offsets, const int32_t* kv_lens, int batch, int n_heads_q,
+                 int n_heads_kv, int head_dim, int dtype, float softmax_scale, int split_len,
+                 int max_splits) {
+  if (!q || !k_cache || !v_cache || !kv_offsets || !kv_lens)
+    return fail(FA_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (batch < 1 || n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "%s: bad batch or head counts", fn);
+  if (!head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "%s: unsupported dtype %d", fn, dtype);
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", fn);
+  if (split_len < 16 || split_len % 16 != 0 || max_splits < 1)
+    return fail(FA_ERR_INVALID_ARG,
+                "%s: split_len must be a positive multiple of 16, max_splits >= 1", fn);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(FA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  if (q_sb < 0 || q_sh < 0 || kv_stride_tok < 0 || kv_stride_head < 0 || q_sb % 8 ||
+      q_sh % 8 || kv_stride_tok % 8 || kv_stride_head % 8)
+    return fail(FA_ERR_INVALID_ARG, "%s: strides must be non-negative multiples of 8", fn);
+  if (max_splits > 2147483647 / 2 || batch > 65535 || n_heads_q > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  return FA_OK;
+}
+
+fa::DecodeArgs decode_args(const void* q, int64_t q_sb, int64_t q_sh, const void* k_cache,
+                           const void* v_cache, int64_t kv_stride_tok, int64_t kv_stride_head,
+                           const int64_t* kv_offsets, const int32_t* kv_lens, int batch,
+                           int n_heads_q, int n_heads_kv, float softmax_scale, int split_len,
+                           int max_splits) {
+  fa::DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.kv_offsets = kv_offsets; a.kv_lens = kv_lens;
+  a.q_sb = q_sb; a.q_sh = q_sh; a.kv_st = kv_stride_tok; a.kv_sh = kv_stride_head;
+  a.batch = batch; a.n_heads_q = n_heads_q; a.n_heads_kv = n_heads_kv;
+  a.split_len = split_len; a.max_splits = max_splits;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
 int fa_decode_split_partial(const void* q, int64_t q_sb, int64_t q_sh,
                             const void* k_cache, const void* v_cache,
                             int64_t kv_stride_tok, int64_t kv_stride_head,
@@ -296,39 +347,67 @@ int fa_decode_split_partial(const void* q, int64_t q_sb, int64_t q_sh,
                             int batch, int n_heads_q, int n_heads_kv, int head_dim, int dtype,
                             float softmax_scale, int split_len, int max_splits,
                             float* part_o, float* part_lse, void* stream) {
-  if (!q || !k_cache || !v_cache || !kv_offsets || !kv_lens || !part_o || !part_lse)
-    return fail(FA_ERR_INVALID_ARG, "fa_decode_split_partial: null pointer argument");
-  if (batch < 1 || n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0)
-    return fail(FA_ERR_INVALID_ARG, "fa_decode_split_partial: bad batch or head counts");
-  if (!head_dim_supported(head_dim))
-    return fail(FA_ERR_UNSUPPORTED, "fa_decode_split_partial: head_dim %d not in {64, 128, 256}",
-                head_dim);
-  if (dtype != FA_F16 && dtype != FA_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "fa_decode_split_partial: unsupported dtype %d", dtype);
-  if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
-    return fail(FA_ERR_INVALID_ARG, "fa_decode_split_partial: softmax_scale must be finite and > 0");
-  if (split_len < 16 || split_len % 16 != 0 || max_splits < 1)
-    return fail(FA_ERR_INVALID_ARG,
-                "fa_decode_split_partial: split_len must be a positive multiple of 16, "
-                "max_splits >= 1");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o))
-    return fail(FA_ERR_INVALID_ARG, "fa_decode_split_partial: misaligned pointer");
-  if (q_sb < 0 || q_sh < 0 || kv_stride_tok < 0 || kv_stride_head < 0 || q_sb % 8 ||
-      q_sh % 8 || kv_stride_tok % 8 || kv_stride_head % 8)
-    return fail(FA_ERR_INVALID_ARG,
-                "fa_decode_split_partial: strides must be non-negative multiples of 8");
-  if (max_splits > 2147483647 / 2 || batch > 65535 || n_heads_q > 65535)
-    return fail(FA_ERR_UNSUPPORTED, "fa_decode_split_partial: grid too large");
-
-  fa::DecodeArgs a;
-  a.q = q; a.k = k_cache; a.v = v_cache; a.kv_offsets = kv_offsets; a.kv_lens = kv_lens;
+  const char* fn = "fa_decode_split_partial";
+  if (!part_o || !part_lse) return fail(FA_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned16(part_o)) return fail(FA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  const int st = check_decode(fn, q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok,
+                              kv_stride_head, kv_offsets, kv_lens, batch, n_heads_q, n_heads_kv,
+                              head_dim, dtype, softmax_scale, split_len, max_splits);
+  if (st != FA_OK) return st;
+  fa::DecodeArgs a = decode_args(q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok, kv_stride_head,
+                                 kv_offsets, kv_lens, batch, n_heads_q, n_heads_kv,
+                                 softmax_scale, split_len, max_splits);
   a.part_o = part_o; a.part_lse = part_lse;
-  a.q_sb = q_sb; a.q_sh = q_sh; a.kv_st = kv_stride_tok; a.kv_sh = kv_stride_head;
-  a.batch = batch; a.n_heads_q = n_heads_q; a.n_heads_kv = n_heads_kv;
-  a.split_len = split_len; a.max_splits = max_splits;
-  a.scale_log2 = softmax_scale * kLog2e;
   return hip_status(fa::launch_decode_partial(a, head_dim, dtype == FA_BF16, (hipStream_t)stream),
                     "fa_decode_split_partial launch");
+}
+
+int fa_decode_fused(const void* q, int64_t q_sb, int64_t q_sh,
+                    const void* k_cache, const void* v_cache,
+                    int64_t kv_stride_tok, int64_t kv_stride_head,
+                    const int64_t* kv_offsets, const int32_t* kv_lens,
+                    int batch, int n_heads_q, int n_heads_kv, int head_dim, int dtype,
+                    float softmax_scale, int split_len, int max_splits,
+                    float* o, float* lse, void* workspace, uint64_t workspace_bytes,
+                    void* stream) {
+  const char* fn = "fa_decode_fused";
+  if (!o || !lse) return fail(FA_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  const int st = check_decode(fn, q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok,
+                              kv_stride_head, kv_offsets, kv_lens, batch, n_heads_q, n_heads_kv,
+                              head_dim, dtype, softmax_scale, split_len, max_splits);
+  if (st != FA_OK) return st;
+  const fa::FusedLayout f =
+      fa::decode_fused_layout(batch, n_heads_q, n_heads_kv, head_dim, max_splits);
+  if (f.n_counters * (int64_t)sizeof(int) > (int64_t)fa::kFusedCounterBytes)
+    return fail(FA_ERR_UNSUPPORTED, "%s: batch * head groups (%lld) above %d", fn,
+                (long long)f.n_counters, (int)(fa::kFusedCounterBytes / sizeof(int)));
+  if (!workspace || workspace_bytes < f.total || ((uintptr_t)workspace & 255u))
+    return fail(FA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned and hold %llu bytes",
+                fn, (unsigned long long)f.total);
+  fa::DecodeArgs a = decode_args(q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok, kv_stride_head,
+                                 kv_offsets, kv_lens, batch, n_heads_q, n_heads_kv,
+                                 softmax_scale, split_len, max_splits);
+  char* ws = (char*)workspace;
+  a.o = o; a.lse = lse;
+  a.counters = (int*)(ws + f.counters);
+  a.wg_lse = (float*)(ws + f.wg_lse);
+  a.wg_o = (float*)(ws + f.wg_o);
+  a.max_wg = f.max_wg;
+  return hip_status(fa::launch_decode_fused(a, head_dim, dtype == FA_BF16, (hipStream_t)stream),
+                    "fa_decode_fused launch");
+}
+
+uint64_t fa_decode_fused_workspace_size(int batch, int n_heads_q, int n_heads_kv, int head_dim,
+                                        int max_splits) {
+  if (batch < 1 || n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0 ||
+      !head_dim_supported(head_dim) || max_splits < 1)
+    return 0;
+  return fa::decode_fused_layout(batch, n_heads_q, n_heads_kv, head_dim, max_splits).total;
+}
+
+int fa_decode_fused_waves(int head_dim, int max_splits) {
+  if (!head_dim_supported(head_dim) || max_splits < 1) return 0;
+  return fa::decode_fused_waves(head_dim, max_splits);
 }
 
 int fa_decode_merge_lse(const float* part_o, const float* part_lse, const int32_t* kv_lens,

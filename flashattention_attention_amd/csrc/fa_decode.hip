@@ -80,11 +80,18 @@ __device__ __forceinline__ float half_hi(unsigned w) {
   else return (float)__builtin_bit_cast(f16x2, w)[1];
 }
 
-// D: head_dim. G: query heads served per wave (a divisor of the GQA group).
+constexpr int lanes_per_row(int d) { return d >= 128 ? 16 : 8; }
+
+// Online softmax of query heads h0 .. h0+G-1 of sequence b over its keys
+// [lo, hi) (lo < hi), by one wave. D: head_dim. G: query heads served per wave
+// (a divisor of the GQA group). On return every lane holds the split's running
+// max m (log2 units), the row sum l and the un-normalized output o relative to
+// base m; lane holds output elements c*EPL .. c*EPL+EPL-1 with c = lane % LPK.
 template <int D, int G, bool BF16>
-__global__ void __launch_bounds__(64)
-decode_partial_kernel(DecodeArgs a) {
-  constexpr int LPK = D >= 128 ? 16 : 8;   // lanes per K/V row
+__device__ __forceinline__ void split_attend(const DecodeArgs& a, int b, int h0, int lo, int hi,
+                                             int lane, float (&m)[G], float (&l)[G],
+                                             float (&o)[G][D / lanes_per_row(D)]) {
+  constexpr int LPK = lanes_per_row(D);    // lanes per K/V row
   constexpr int EPL = D / LPK;             // elements per lane: 8 or 16
   constexpr int W = EPL / 8;               // 16-byte loads per row per lane
   constexpr int KPS = 64 / LPK;            // rows per load step: 4 or 8
@@ -93,15 +100,7 @@ decode_partial_kernel(DecodeArgs a) {
   constexpr int NB = D == 256 ? (G > 4 ? 2 : 4) : (G > 4 ? 4 : 8);
   constexpr int BK = KPS * NB;             // rows per block
 
-  const int lane = threadIdx.x;
-  const int h0 = blockIdx.x * G;   // head groups fastest: the waves reading the
-  const int s = blockIdx.y;        // same tokens' rows are dispatched together
-  const int b = blockIdx.z;
   const int hk = h0 / (a.n_heads_q / a.n_heads_kv);
-  const int L = a.kv_lens[b];
-  const int lo = s * a.split_len;
-  if (L < 1 || lo >= L) return;          // empty split: nothing read or written
-  const int hi = min(L, lo + a.split_len);
   const int slot = lane / LPK;           // which of the KPS rows of a step
   const int c = lane % LPK;              // which EPL-element chunk of the row
 
@@ -134,7 +133,6 @@ decode_partial_kernel(DecodeArgs a) {
     }
   };
 
-  float m[G], l[G], o[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -1e30f;
@@ -207,7 +205,7 @@ decode_partial_kernel(DecodeArgs a) {
     compute_block(start + BK, kb, vb);
   }
 
-  // Sum the row slots (m is the same in every lane), then write the partial.
+  // Sum the row slots (m is the same in every lane).
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -217,6 +215,27 @@ decode_partial_kernel(DecodeArgs a) {
       for (int e = 0; e < EPL; ++e) o[g][e] += __shfl_xor(o[g][e], x);
     }
   }
+}
+
+// One wave per (sequence, group of G query heads, split): the split's
+// normalized partial output and its natural-log LSE.
+template <int D, int G, bool BF16>
+__global__ void __launch_bounds__(64)
+decode_partial_kernel(DecodeArgs a) {
+  constexpr int LPK = lanes_per_row(D);
+  constexpr int EPL = D / LPK;
+  const int lane = threadIdx.x;
+  const int h0 = blockIdx.x * G;   // head groups fastest: the waves reading the
+  const int s = blockIdx.y;        // same tokens' rows are dispatched together
+  const int b = blockIdx.z;
+  const int L = a.kv_lens[b];
+  const int lo = s * a.split_len;
+  if (L < 1 || lo >= L) return;          // empty split: nothing read or written
+  const int hi = min(L, lo + a.split_len);
+  const int slot = lane / LPK;
+  const int c = lane % LPK;
+  float m[G], l[G], o[G][EPL];
+  split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
   if (slot == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -232,30 +251,17 @@ decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// One wave per (sequence, query head). Split LSEs are read lane-parallel and
-// reduced across the wave; the weighted sum of the split outputs runs over
-// the splits in index order with the loads of several splits in flight.
+// Merge of ns >= 1 normalized partials of one query head by one wave: pl[j]
+// is partial j's natural-log LSE, po + j*D its output row. Split LSEs are read
+// lane-parallel and reduced across the wave; the weighted sum of the partial
+// outputs runs over the partials in index order with the loads of several
+// partials in flight. Writes out[0..D) and *lse_out.
 template <int D>
-__global__ void __launch_bounds__(64)
-decode_merge_kernel(MergeArgs a) {
+__device__ __forceinline__ void merge_head(const float* pl, const float* po_row0, int ns,
+                                           int lane, float* out, float* lse_out) {
   constexpr int EPL = D / 64;
-  constexpr int U = 32;                    // splits in flight per step
-  const int lane = threadIdx.x;
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int64_t bh = (int64_t)b * a.n_heads_q + h;
-  float* out = a.o + bh * D;
-  const int L = a.kv_lens[b];
-  const int ns = L < 1 ? 0 : (L + a.split_len - 1) / a.split_len;
-  if (ns < 1 || ns > a.max_splits) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) out[lane * EPL + e] = __builtin_nanf("");
-    if (lane == 0) a.lse[bh] = __builtin_nanf("");
-    return;
-  }
-  const float* pl = a.part_lse + bh * a.max_splits;
-  const float* po = a.part_o + bh * a.max_splits * D + lane * EPL;
-
+  constexpr int U = 32;                    // partials in flight per step
+  const float* po = po_row0 + lane * EPL;
   float M = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += 64)
     if (s0 + lane < ns) M = fmaxf(M, pl[s0 + lane]);
@@ -292,7 +298,248 @@ decode_merge_kernel(MergeArgs a) {
   const float inv = 1.0f / wsum;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) out[lane * EPL + e] = acc[e] * inv;
-  if (lane == 0) a.lse[bh] = M + __logf(wsum);
+  if (lane == 0) *lse_out = M + __logf(wsum);
+}
+
+// NaN output row and LSE: the mark of a sequence whose length breaks the plan.
+template <int D>
+__device__ __forceinline__ void nan_head(int lane, float* out, float* lse_out) {
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) out[lane * (D / 64) + e] = __builtin_nanf("");
+  if (lane == 0) *lse_out = __builtin_nanf("");
+}
+
+// One wave per (sequence, query head).
+template <int D>
+__global__ void __launch_bounds__(64)
+decode_merge_kernel(MergeArgs a) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t bh = (int64_t)b * a.n_heads_q + h;
+  const int L = a.kv_lens[b];
+  const int ns = L < 1 ? 0 : (L + a.split_len - 1) / a.split_len;
+  if (ns < 1 || ns > a.max_splits)
+    nan_head<D>(lane, a.o + bh * D, a.lse + bh);
+  else
+    merge_head<D>(a.part_lse + bh * a.max_splits, a.part_o + bh * a.max_splits * D, ns, lane,
+                  a.o + bh * D, a.lse + bh);
+}
+
+// Single-launch decode. A work-group of NW waves takes NW consecutive splits
+// of one (sequence, head group); each wave runs its split as above, and the
+// work-group merges the NW results through LDS (max-shifted weights, waves in
+// split order). When one work-group covers every split of the sequence, that
+// merge is the output. Otherwise each work-group stores its merged partial
+// and LSE, and the last work-group of the (sequence, head group) to finish
+// (an agent-scope counter; no work-group ever waits for another) merges those
+// partials in index order and resets the counter to zero. The result is a
+// fixed function of the split plan, so repeated runs are byte-identical.
+template <int D, int G, bool BF16, int NW>
+__global__ void __launch_bounds__(64 * NW)
+decode_fused_kernel(DecodeArgs a) {
+  constexpr int LPK = lanes_per_row(D);
+  constexpr int EPL = D / LPK;
+  constexpr int NT = 64 * NW;
+  __shared__ float so[NW][G][D];
+  __shared__ float sm[NW][G], sl[NW][G];
+  __shared__ int is_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hg = blockIdx.x, h0 = hg * G, y = blockIdx.y, b = blockIdx.z;
+  const int L = a.kv_lens[b];
+  const int ns = L < 1 ? 0 : (L + a.split_len - 1) / a.split_len;
+  const bool bad = ns < 1 || ns > a.max_splits;
+  const int nwg = bad ? 0 : (ns + NW - 1) / NW;              // work-groups with splits
+  const int nvalid = bad ? 0 : min(NW, max(0, ns - y * NW));  // splits of this one
+  const bool single = a.max_wg == 1;
+
+  if (wave < nvalid) {
+    const int lo = (y * NW + wave) * a.split_len;
+    const int hi = min(L, lo + a.split_len);
+    float m[G], l[G], o[G][EPL];
+    split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
+    if (lane < LPK) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          *(f32x4*)&so[wave][g][lane * EPL + e] =
+              f32x4{o[g][e], o[g][e + 1], o[g][e + 2], o[g][e + 3]};
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        sm[wave][g] = m[g];
+        sl[wave][g] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t bh0 = (int64_t)b * a.n_heads_q + h0;
+  if (nvalid > 0) {
+    for (int e = tid; e < G * D; e += NT) {
+      const int g = e / D, d = e % D;
+      float M = sm[0][g];
+      for (int w = 1; w < nvalid; ++w) M = fmaxf(M, sm[w][g]);
+      float lsum = 0.0f, acc = 0.0f;
+      for (int w = 0; w < nvalid; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm[w][g] - M);
+        lsum = __builtin_fmaf(f, sl[w][g], lsum);
+        acc = __builtin_fmaf(f, so[w][g][d], acc);
+      }
+      const float out = acc / lsum;                 // every split has a key: lsum >= 1
+      const float lse = (M + __log2f(lsum)) * kLn2;
+      if (single) {
+        a.o[(bh0 + g) * D + d] = out;
+        if (d == 0) a.lse[bh0 + g] = lse;
+      } else {   // agent-scope stores: written through to memory, seen by every XCD
+        __hip_atomic_store(&a.wg_o[((bh0 + g) * a.max_wg + y) * D + d], out, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0)
+          __hip_atomic_store(&a.wg_lse[(bh0 + g) * a.max_wg + y], lse, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (single) {
+    if (bad)
+      for (int e = tid; e < G * D; e += NT) {
+        a.o[(bh0 + e / D) * D + e % D] = __builtin_nanf("");
+        if (e % D == 0) a.lse[bh0 + e / D] = __builtin_nanf("");
+      }
+    return;
+  }
+
+  // Count this work-group once its partial has reached memory, and let the
+  // last one merge. The partial went out as agent-scope stores, so waiting for
+  // their completion publishes it; an agent-scope release fence would instead
+  // write back the whole L2 of this XCD from every work-group.
+  int* counter = a.counters + (int64_t)b * gridDim.x + hg;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (int)gridDim.y - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // drop stale cached partials
+
+  // Wave w merges heads w, w + NW, ... of the group, all of them at once so
+  // that their loads are in flight together (as merge_head does for one).
+  constexpr int GH = (G + NW - 1) / NW;          // heads per wave
+  constexpr int EPL2 = D / 64;                   // output elements per lane
+  constexpr int U = GH * EPL2 <= 64 ? 64 / (GH * EPL2) : 1;   // partial rows in flight
+  const float* pl[GH];
+  const float* po[GH];
+  bool hv[GH];
+#pragma unroll
+  for (int i = 0; i < GH; ++i) {
+    const int g = wave + i * NW;
+    hv[i] = g < G;
+    const int64_t bh = bh0 + (hv[i] ? g : 0);
+    pl[i] = a.wg_lse + bh * a.max_wg;
+    po[i] = a.wg_o + bh * a.max_wg * D + lane * EPL2;
+    if (bad && hv[i]) nan_head<D>(lane, a.o + bh * D, a.lse + bh);
+  }
+  if (!bad && nwg <= U) {
+    // Common case: every partial row and LSE is requested in one round.
+    float v[GH][U][EPL2], lv[GH];
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      lv[i] = pl[i][min(lane, nwg - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < EPL2; ++e) v[i][u][e] = po[i][(int64_t)min(u, nwg - 1) * D + e];
+    }
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      if (!hv[i]) continue;
+      float M = lane < nwg ? lv[i] : -INFINITY;
+#pragma unroll
+      for (int x = 1; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
+      const float wl = lane < nwg ? __expf(lv[i] - M) : 0.0f;
+      float acc[EPL2];
+#pragma unroll
+      for (int e = 0; e < EPL2; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u < nwg) {
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+#pragma unroll
+          for (int e = 0; e < EPL2; ++e) acc[e] = __builtin_fmaf(w, v[i][u][e], acc[e]);
+        }
+      float wsum = wl;
+#pragma unroll
+      for (int x = 1; x < 64; x *= 2) wsum += __shfl_xor(wsum, x);
+      const int64_t bh = bh0 + wave + i * NW;
+      const float inv = 1.0f / wsum;
+#pragma unroll
+      for (int e = 0; e < EPL2; ++e) a.o[bh * D + lane * EPL2 + e] = acc[e] * inv;
+      if (lane == 0) a.lse[bh] = M + __logf(wsum);
+    }
+  } else if (!bad) {
+    float M[GH], wsum[GH], acc[GH][EPL2];
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      M[i] = -INFINITY;
+      wsum[i] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL2; ++e) acc[i][e] = 0.0f;
+    }
+    for (int j0 = 0; j0 < nwg; j0 += 64)
+#pragma unroll
+      for (int i = 0; i < GH; ++i)
+        if (j0 + lane < nwg) M[i] = fmaxf(M[i], pl[i][j0 + lane]);
+#pragma unroll
+    for (int i = 0; i < GH; ++i)
+#pragma unroll
+      for (int x = 1; x < 64; x *= 2) M[i] = fmaxf(M[i], __shfl_xor(M[i], x));
+    for (int j0 = 0; j0 < nwg; j0 += 64) {
+      float wl[GH];
+#pragma unroll
+      for (int i = 0; i < GH; ++i) {
+        wl[i] = j0 + lane < nwg ? __expf(pl[i][j0 + lane] - M[i]) : 0.0f;
+        wsum[i] += wl[i];
+      }
+      const int n = min(64, nwg - j0);
+      for (int j = 0; j < n; j += U) {
+        float v[GH][U][EPL2];
+#pragma unroll
+        for (int i = 0; i < GH; ++i)
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int sj = j0 + min(j + u, n - 1);
+#pragma unroll
+            for (int e = 0; e < EPL2; ++e) v[i][u][e] = po[i][(int64_t)sj * D + e];
+          }
+#pragma unroll
+        for (int i = 0; i < GH; ++i)
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (j + u < n) {
+              const float w =
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl[i]), j + u));
+#pragma unroll
+              for (int e = 0; e < EPL2; ++e) acc[i][e] = __builtin_fmaf(w, v[i][u][e], acc[i][e]);
+            }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      if (!hv[i]) continue;
+#pragma unroll
+      for (int x = 1; x < 64; x *= 2) wsum[i] += __shfl_xor(wsum[i], x);
+      const int64_t bh = bh0 + wave + i * NW;
+      const float inv = 1.0f / wsum[i];
+#pragma unroll
+      for (int e = 0; e < EPL2; ++e) a.o[bh * D + lane * EPL2 + e] = acc[i][e] * inv;
+      if (lane == 0) a.lse[bh] = M[i] + __logf(wsum[i]);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, bool BF16>
@@ -309,7 +556,77 @@ hipError_t launch_partial_d(const DecodeArgs& a, int g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool BF16, int NW>
+hipError_t launch_fused_dw(const DecodeArgs& a, int g, hipStream_t stream) {
+  const dim3 grid(a.n_heads_q / g, a.max_wg, a.batch);
+  switch (g) {
+#define FA_CASE(G)                                                                           \
+  case G:                                                                                    \
+    hipLaunchKernelGGL((decode_fused_kernel<D, G, BF16, NW>), grid, dim3(64 * NW), 0, stream, \
+                       a);                                                                   \
+    break;
+    FA_CASE(1) FA_CASE(2) FA_CASE(3) FA_CASE(4) FA_CASE(5) FA_CASE(6) FA_CASE(7) FA_CASE(8)
+#undef FA_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_fused_d(const DecodeArgs& a, int g, int nw, hipStream_t stream) {
+  switch (nw) {
+    case 1: return launch_fused_dw<D, BF16, 1>(a, g, stream);
+    case 4: return launch_fused_dw<D, BF16, 4>(a, g, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+// Few splits per sequence (long splits, bandwidth-bound): one wave per
+// work-group, so no compute unit slot waits on a sibling wave with no split;
+// many (short, latency-bound splits): merge groups of 4 on chip first, so the
+// last work-group merges few partials (measured at 28/4 heads and 1641
+// tokens: 4 waves beat 2 and 8, which packs the latency-bound waves onto too
+// few compute units).
+int decode_fused_waves(int head_dim, int max_splits) {
+  (void)head_dim;
+  return max_splits <= 16 ? 1 : 4;
+}
+
+FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int head_dim,
+                                int max_splits) {
+  FusedLayout f{};
+  const int g = decode_heads_per_wave(n_heads_q / n_heads_kv);
+  f.waves = decode_fused_waves(head_dim, max_splits);
+  f.max_wg = (max_splits + f.waves - 1) / f.waves;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  // The counters sit in a fixed region at the start, whatever the shape, so a
+  // workspace can serve calls of different shapes: no call's partials ever
+  // land where another shape keeps its (zero between calls) counters.
+  f.counters = 0;
+  f.n_counters = (int64_t)batch * (n_heads_q / g);
+  f.wg_lse = kFusedCounterBytes;
+  f.wg_o = f.wg_lse + up((size_t)batch * n_heads_q * f.max_wg * sizeof(float));
+  f.total = f.wg_o + up((size_t)batch * n_heads_q * f.max_wg * head_dim * sizeof(float));
+  return f;
+}
+
+hipError_t launch_decode_fused(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream) {
+  const int g = decode_heads_per_wave(a.n_heads_q / a.n_heads_kv);
+  const int nw = decode_fused_waves(head_dim, a.max_splits);
+  if ((a.max_splits + nw - 1) / nw != a.max_wg) return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 64: return bf16 ? launch_fused_d<64, true>(a, g, nw, stream)
+                         : launch_fused_d<64, false>(a, g, nw, stream);
+    case 128: return bf16 ? launch_fused_d<128, true>(a, g, nw, stream)
+                          : launch_fused_d<128, false>(a, g, nw, stream);
+    case 256: return bf16 ? launch_fused_d<256, true>(a, g, nw, stream)
+                          : launch_fused_d<256, false>(a, g, nw, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 // Heads served per wave: the largest divisor of the GQA group that is <= 8.
 int decode_heads_per_wave(int group) {

@@ -38,6 +38,13 @@ struct DecodeArgs {
   int batch, n_heads_q, n_heads_kv;
   int split_len, max_splits;
   float scale_log2;
+  // single-launch form only
+  float* o;          // [batch, n_heads_q, head_dim]
+  float* lse;        // [batch, n_heads_q]
+  int* counters;     // [batch, n_heads_q / heads_per_wave], zero between calls
+  float* wg_o;       // [batch, n_heads_q, max_wg, head_dim]
+  float* wg_lse;     // [batch, n_heads_q, max_wg]
+  int max_wg;        // work-groups per (sequence, head group)
 };
 
 struct MergeArgs {
@@ -68,6 +75,19 @@ hipError_t launch_prefill_attn(const PrefillArgs& a, const VtArgs& w, int head_d
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                                  hipStream_t stream);
 hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode_fused(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+
+// Splits (one per wave) merged inside one work-group of the single-launch decode.
+int decode_fused_waves(int head_dim, int max_splits);
+// Workspace of the single-launch decode, and the offsets of its parts.
+constexpr size_t kFusedCounterBytes = 65536;   // room for 16384 arrival counters
+struct FusedLayout {
+  size_t counters, wg_lse, wg_o, total;
+  int64_t n_counters;
+  int waves, max_wg;
+};
+FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int head_dim,
+                                int max_splits);
 
 // Geometry of the decode partial kernel, for the split planner.
 int decode_heads_per_wave(int group);

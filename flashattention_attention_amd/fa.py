@@ -43,6 +43,11 @@ _SIGNATURES = {
                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp],
                                 _i32),
     "fa_decode_merge_lse": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
+    "fa_decode_fused": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
+                         _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp,
+                         _vp, ctypes.c_uint64, _vp], _i32),
+    "fa_decode_fused_workspace_size": ([_i32, _i32, _i32, _i32, _i32], ctypes.c_uint64),
+    "fa_decode_fused_waves": ([_i32, _i32], _i32),
     "fa_status_string": ([_i32], ctypes.c_char_p),
     "fa_last_error": ([], ctypes.c_char_p),
 }
@@ -311,23 +316,9 @@ def decode_split_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     Returns part_o fp32 [B,Hq,max_splits,D] and part_lse fp32 [B,Hq,max_splits]
     (entries of empty splits are left untouched).
     """
-    dev = _on_gpu(q, k_cache, v_cache, kv_offsets, kv_lens)
-    if q.dim() != 3 or k_cache.dim() != 3 or k_cache.shape != v_cache.shape:
-        raise FAError("q must be [B,Hq,D] and the caches [T,Hkv,D] of equal shape")
-    if k_cache.stride() != v_cache.stride():
-        raise FAError("k_cache and v_cache must share strides")
-    if not (q.dtype == k_cache.dtype == v_cache.dtype):
-        raise FAError("q and the caches must share a dtype")
-    if kv_offsets.dtype != torch.int64 or kv_lens.dtype != torch.int32:
-        raise FAError("kv_offsets must be int64 and kv_lens int32")
-    if q.stride(2) != 1 or k_cache.stride(2) != 1:
-        raise FAError("head_dim must be contiguous")
+    dev = _check_decode_inputs(q, k_cache, v_cache, kv_offsets, kv_lens)
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
-    if k_cache.shape[2] != D or kv_offsets.shape != (B,) or kv_lens.shape != (B,):
-        raise FAError("shape mismatch between q, caches, kv_offsets and kv_lens")
-    if not (kv_offsets.is_contiguous() and kv_lens.is_contiguous()):
-        raise FAError("kv_offsets and kv_lens must be contiguous")
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
     if part_o is None:
         part_o = torch.empty((B, Hq, max_splits, D), dtype=torch.float32, device=dev)
@@ -345,6 +336,72 @@ def decode_split_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         part_o.data_ptr(), part_lse.data_ptr(), _stream(dev)),
         (q, k_cache, v_cache, kv_offsets, kv_lens, part_o, part_lse), prepare)
     return call if prepare else (part_o, part_lse)
+
+
+def _check_decode_inputs(q, k_cache, v_cache, kv_offsets, kv_lens):
+    dev = _on_gpu(q, k_cache, v_cache, kv_offsets, kv_lens)
+    if q.dim() != 3 or k_cache.dim() != 3 or k_cache.shape != v_cache.shape:
+        raise FAError("q must be [B,Hq,D] and the caches [T,Hkv,D] of equal shape")
+    if k_cache.stride() != v_cache.stride():
+        raise FAError("k_cache and v_cache must share strides")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise FAError("q and the caches must share a dtype")
+    if kv_offsets.dtype != torch.int64 or kv_lens.dtype != torch.int32:
+        raise FAError("kv_offsets must be int64 and kv_lens int32")
+    if q.stride(2) != 1 or k_cache.stride(2) != 1:
+        raise FAError("head_dim must be contiguous")
+    B, Hq, D = q.shape
+    if k_cache.shape[2] != D or kv_offsets.shape != (B,) or kv_lens.shape != (B,):
+        raise FAError("shape mismatch between q, caches, kv_offsets and kv_lens")
+    if not (kv_offsets.is_contiguous() and kv_lens.is_contiguous()):
+        raise FAError("kv_offsets and kv_lens must be contiguous")
+    return dev
+
+
+def decode_fused_workspace_size(batch: int, n_heads_q: int, n_heads_kv: int, head_dim: int,
+                                max_splits: int) -> int:
+    """Bytes of (zero-filled) workspace fa_decode_fused needs."""
+    return int(load_library().fa_decode_fused_workspace_size(batch, n_heads_q, n_heads_kv,
+                                                             head_dim, max_splits))
+
+
+def decode_fused(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 kv_offsets: torch.Tensor, kv_lens: torch.Tensor, *, split_len: int,
+                 max_splits: int, softmax_scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, prepare: bool = False):
+    """Split-KV decode in one launch. Same inputs as decode_split_partial; returns
+    o fp32 [B,Hq,D] and lse fp32 [B,Hq] (or, with prepare=True, a callable that
+    repeats the call). ``workspace``: a uint8 GPU tensor of at least
+    decode_fused_workspace_size(...) bytes that was zero-filled before its
+    first use (torch.zeros); one is allocated when omitted."""
+    dev = _check_decode_inputs(q, k_cache, v_cache, kv_offsets, kv_lens)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
+    need = decode_fused_workspace_size(B, Hq, Hkv, D, max_splits)
+    if workspace is None:
+        workspace = torch.zeros(max(1, need), dtype=torch.uint8, device=dev)
+    _on_gpu(workspace)
+    if workspace.numel() * workspace.element_size() < need:
+        raise FAError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _on_gpu(out, lse)
+    if out.shape != (B, Hq, D) or lse.shape != (B, Hq) or not out.is_contiguous() \
+            or not lse.is_contiguous() or out.dtype != torch.float32 \
+            or lse.dtype != torch.float32:
+        raise FAError("out / lse must be contiguous fp32 [B,Hq,D] / [B,Hq]")
+    call = _issue("fa_decode_fused", (
+        q.data_ptr(), q.stride(0), q.stride(1), k_cache.data_ptr(), v_cache.data_ptr(),
+        k_cache.stride(0), k_cache.stride(1), kv_offsets.data_ptr(), kv_lens.data_ptr(),
+        B, Hq, Hkv, D, _dtype_code(q), scale, split_len, max_splits,
+        out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(dev)),
+        (q, k_cache, v_cache, kv_offsets, kv_lens, out, lse, workspace), prepare)
+    return call if prepare else (out, lse)
 
 
 def decode_merge_lse(part_o: torch.Tensor, part_lse: torch.Tensor, kv_lens: torch.Tensor, *,

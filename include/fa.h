@@ -234,6 +234,53 @@ int fa_decode_merge_lse(const float* part_o, const float* part_lse, const int32_
                         int batch, int n_heads_q, int head_dim, int split_len, int max_splits,
                         float* o, float* lse, void* stream);
 
+/*
+ * fa_decode_fused — split-KV decode in one launch (partials and their merge).
+ *
+ * Source: as fa_decode_split_partial and fa_decode_merge_lse; "STAGE_D.md —
+ * FMHA Kernel Development", D5c (fuse the passes into one kernel launch).
+ *
+ * Computes what fa_decode_split_partial followed by fa_decode_merge_lse
+ * computes (same arguments, same split partition, o and lse as written by the
+ * merge), in one kernel: each work-group of W = fa_decode_fused_waves(head_dim,
+ * max_splits) waves (1 when max_splits <= 16, else 4)
+ * takes W consecutive splits of one sequence and merges them on chip; when
+ * one work-group covers every split of a sequence its merge is the output,
+ * otherwise the last work-group of the sequence to finish merges the
+ * work-group partials (in index order, so the result is a fixed function of
+ * split_len and max_splits and repeated runs are byte-identical; the summation
+ * order differs from the two-launch form, which agrees to rounding).
+ *
+ * workspace: caller-owned device memory of at least
+ * fa_decode_fused_workspace_size(batch, n_heads_q, n_heads_kv, head_dim,
+ * max_splits) bytes, 256-byte aligned, ZERO-FILLED before its first use. Its
+ * first 64 KiB hold arrival counters (one per sequence and group of query
+ * heads served together, at most 16384 per call: larger batches return
+ * FA_ERR_UNSUPPORTED) and every call returns them to zero when it completes,
+ * so one workspace serves any sequence of calls, of any shapes it is large
+ * enough for. Calls that overlap in time must not share a workspace. A
+ * sequence with
+ * L_b < 1 or ceil(L_b / split_len) > max_splits gets NaN in o and lse.
+ * Validation and supported set as in fa_decode_split_partial.
+ */
+int fa_decode_fused(const void* q, int64_t q_sb, int64_t q_sh,
+                    const void* k_cache, const void* v_cache,
+                    int64_t kv_stride_tok, int64_t kv_stride_head,
+                    const int64_t* kv_offsets, const int32_t* kv_lens,
+                    int batch, int n_heads_q, int n_heads_kv, int head_dim, int dtype,
+                    float softmax_scale, int split_len, int max_splits,
+                    float* o, float* lse, void* workspace, uint64_t workspace_bytes,
+                    void* stream);
+
+/*
+ * fa_decode_fused_workspace_size — bytes of workspace fa_decode_fused needs
+ * (0 for invalid sizes). fa_decode_fused_waves — splits one work-group of
+ * fa_decode_fused merges on chip (0 for invalid sizes). Host only.
+ */
+uint64_t fa_decode_fused_workspace_size(int batch, int n_heads_q, int n_heads_kv, int head_dim,
+                                        int max_splits);
+int fa_decode_fused_waves(int head_dim, int max_splits);
+
 /* Static text for a status code. */
 const char* fa_status_string(int status);
 

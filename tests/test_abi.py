@@ -24,8 +24,9 @@ def test_exports_every_declared_symbol():
     names = fa.declared_functions()
     assert set(names) == {"fa_prefill_fwd", "fa_prefill_pack_v", "fa_prefill_fwd_packed",
                           "fa_prefill_workspace_size", "fa_decode_plan",
-                          "fa_decode_split_partial", "fa_decode_merge_lse", "fa_status_string",
-                          "fa_last_error"}
+                          "fa_decode_split_partial", "fa_decode_merge_lse", "fa_decode_fused",
+                          "fa_decode_fused_workspace_size", "fa_decode_fused_waves",
+                          "fa_status_string", "fa_last_error"}
     lib = ctypes.CDLL(fa.library_path())
     for name in names:
         assert hasattr(lib, name), name
@@ -179,6 +180,44 @@ def test_decode_merge_validation(kw, status):
     st = lib.fa_decode_merge_lse(b["po"], b["pl"], b["lens"], b["B"], b["Hq"], b["D"],
                                  b["split"], b["ms"], b["o"], b["lse"], None)
     assert st == status
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lens=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
+    (dict(Hkv=3), 1), (dict(D=80), 2), (dict(dtype=2), 2), (dict(split=24), 1), (dict(ms=0), 1),
+    (dict(scale=0.0), 1), (dict(ws=None), 1), (dict(wsb=100), 1), (dict(ws=ALIGNED + 64), 1),
+    (dict(B=16385, Hq=2, Hkv=2), 2),
+])
+def test_decode_fused_validation(kw, status):
+    b = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, offs=ALIGNED, lens=ALIGNED, o=ALIGNED, lse=ALIGNED,
+             B=1, Hq=4, Hkv=2, D=128, dtype=0, scale=0.1, split=32, ms=4, ws=ALIGNED, wsb=1 << 40)
+    b.update(kw)
+    lib = fa.load_library()
+    st = lib.fa_decode_fused(b["q"], 512, 128, b["k"], b["v"], 256, 128, b["offs"], b["lens"],
+                             b["B"], b["Hq"], b["Hkv"], b["D"], b["dtype"], b["scale"],
+                             b["split"], b["ms"], b["o"], b["lse"], b["ws"], b["wsb"], None)
+    assert st == status, lib.fa_last_error()
+
+
+def test_decode_fused_workspace_size():
+    lib = fa.load_library()
+    assert lib.fa_decode_fused_waves(128, 52) == 4 and lib.fa_decode_fused_waves(256, 52) == 4
+    assert lib.fa_decode_fused_waves(128, 16) == 1 and lib.fa_decode_fused_waves(96, 4) == 0
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    # 1 sequence, 28/4 heads (7 per wave -> 4 head groups), 52 splits -> 13 work-groups
+    want = 65536 + up(28 * 13 * 4) + up(28 * 13 * 128 * 4)     # fixed counter region first
+    assert lib.fa_decode_fused_workspace_size(1, 28, 4, 128, 52) == want
+    # 32 sequences, 32/8 heads (4 per wave), head_dim 256, 40 splits -> 4 per work-group
+    want = 65536 + up(32 * 32 * 10 * 4) + up(32 * 32 * 10 * 256 * 4)
+    assert lib.fa_decode_fused_workspace_size(32, 32, 8, 256, 40) == want
+    # 13 splits: one per work-group
+    want = 65536 + up(32 * 32 * 13 * 4) + up(32 * 32 * 13 * 128 * 4)
+    assert lib.fa_decode_fused_workspace_size(32, 32, 8, 128, 13) == want
+    assert lib.fa_decode_fused_workspace_size(1, 4, 3, 128, 4) == 0
+    assert lib.fa_decode_fused_workspace_size(1, 4, 2, 96, 4) == 0
 
 
 def test_workspace_size():
