@@ -52,6 +52,17 @@ every enabled condition admits it:
 A row with no visible key has no softmax; the reading taken (as for an empty
 decode split) is O = 0, row_sum = 0, LSE = row_max = -inf.
 
+Sink logits ("STAGE_D.md — FMHA Kernel Development", D5: a sliding-window
+pass and a sink merged through their LSEs, the sink merge folded into the
+kernel epilogue in D5d). The pages do not define the sink. The reading taken
+is a per-head logit sigma_h that joins every row's softmax as one more term
+with no value row, i.e. a branch whose LSE is sigma_h and whose output is 0:
+    m_i = max(max_j s_ij, sigma_h),  l_i = sum_j exp(s_ij - m_i) + exp(sigma_h - m_i),
+    U_i = sum_j exp(s_ij - m_i) v_j,  O_i = U_i / l_i,  LSE_i = m_i + ln(l_i).
+A row with no visible key then has O = 0, LSE = sigma_h. Merging the results
+of passes over disjoint key sets (merge_branches) is the same max-shifted
+LSE merge as for the decode splits.
+
 This is the two-pass form (max first, then exponentials), not an online
 softmax, so it is the definition rather than an algorithm that reaches it.
 """
@@ -89,14 +100,17 @@ def _as_f64(x, dtype: Optional[str]) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                q_pos: Optional[np.ndarray], visible: Optional[np.ndarray] = None) -> dict:
+                q_pos: Optional[np.ndarray], visible: Optional[np.ndarray] = None,
+                sink: Optional[float] = None) -> dict:
     """Softmax attention of query rows over keys 0..Skv-1, fp64.
 
     q_rows [R, D]; k, v [Skv, D]; q_pos [R] absolute query positions (causal:
     key j is visible iff j <= q_pos), or None for no causal mask; visible
-    [R, Skv] an optional further boolean mask (True = visible).
+    [R, Skv] an optional further boolean mask (True = visible); sink an
+    optional sink logit (one more softmax term with no value row).
     Returns o, lse, row_sum (l), o_unnorm (U), row_max (m), each per row; a row
-    with no visible key gets o = o_unnorm = 0, row_sum = 0, lse = row_max = -inf.
+    with no visible key and no sink gets o = o_unnorm = 0, row_sum = 0,
+    lse = row_max = -inf.
     """
     scores = (q_rows @ k.T) * float(scale)                       # s_ij
     if q_pos is not None:
@@ -105,9 +119,13 @@ def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     if visible is not None:
         scores = np.where(visible, scores, -np.inf)
     m = scores.max(axis=1)                                       # m_i
+    if sink is not None:
+        m = np.maximum(m, float(sink))
     empty = np.isneginf(m)
     p = np.exp(scores - np.where(empty, 0.0, m)[:, None])        # masked -> exp(-inf) = 0
     l = p.sum(axis=1)                                            # l_i
+    if sink is not None:
+        l = l + np.exp(float(sink) - np.where(empty, 0.0, m))
     u = p @ v                                                    # U_i
     with np.errstate(divide="ignore", invalid="ignore"):
         o = np.where(empty[:, None], 0.0, u / np.where(empty, 1.0, l)[:, None])
@@ -116,14 +134,16 @@ def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def prefill(q, k, v, *, scale: float, causal: bool = True, dtype: Optional[str] = None,
-            rows: Optional[Iterable[int]] = None, kv_lens=None, window: int = 0) -> dict:
+            rows: Optional[Iterable[int]] = None, kv_lens=None, window: int = 0,
+            sink_logits=None) -> dict:
     """Attention forward for the whole problem (or for the query rows listed).
 
     q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D]; half bit patterns when ``dtype``
     is given, real numbers otherwise. ``scale`` is the fp32 softmax scale the
     GPU receives; it is widened to float64 unchanged. ``kv_lens`` [B] (valid KV
     length per sequence) and ``window`` (> 0: sliding window) add the masks
-    described in the module docstring.
+    described in the module docstring; ``sink_logits`` [Hq] adds a per-head
+    sink logit.
 
     Returns float64 arrays: o and o_unnorm [B, R, Hq, Dv]; lse, row_sum and
     row_max [B, Hq, R], where R is Sq or len(rows).
@@ -154,7 +174,7 @@ def prefill(q, k, v, *, scale: float, causal: bool = True, dtype: Optional[str] 
         for h in range(Hq):
             hk = h // group
             r = attend_rows(qf[b, rows, h, :], kf[b, :, hk, :], vf[b, :, hk, :], scale, q_pos,
-                            visible)
+                            visible, None if sink_logits is None else float(sink_logits[h]))
             out["o"][b, :, h, :] = r["o"]
             out["o_unnorm"][b, :, h, :] = r["o_unnorm"]
             out["lse"][b, h, :] = r["lse"]
@@ -256,4 +276,27 @@ def merge_partials(part_o, part_lse, n_splits) -> dict:
             w = np.exp(ls - M)
             o[b, h] = (w[:, None] * part_o[b, h, :n]).sum(axis=0) / w.sum()
             lse[b, h] = M + math.log(w.sum())
+    return {"o": o, "lse": lse}
+
+
+def merge_branches(o_parts, lse_parts) -> dict:
+    """Merge the results of attention passes over disjoint key sets.
+
+    o_parts: list of normalized outputs [..., D]; lse_parts: list of their
+    LSEs [...] (same leading shape). Elementwise over the leading shape, the
+    max-shifted LSE merge M = max_b LSE_b, w_b = exp(LSE_b - M),
+    O = sum_b w_b O_b / sum_b w_b, LSE = M + ln(sum_b w_b). Where every LSE is
+    -inf (no key in any pass) the result is O = 0, LSE = -inf. A sink logit
+    sigma enters as a branch with O = 0 and LSE = sigma.
+    """
+    ls = np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts])      # [n, ...]
+    os_ = np.stack([np.asarray(x, dtype=np.float64) for x in o_parts])       # [n, ..., D]
+    M = ls.max(axis=0)
+    empty = np.isneginf(M)
+    w = np.exp(ls - np.where(empty, 0.0, M)[None])
+    wsum = w.sum(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.where(empty[..., None], 0.0,
+                     (w[..., None] * os_).sum(axis=0) / np.where(empty, 1.0, wsum)[..., None])
+        lse = np.where(empty, -np.inf, M + np.log(np.where(empty, 1.0, wsum)))
     return {"o": o, "lse": lse}

@@ -589,3 +589,120 @@ def test_brute_force_decimal_masks(causal, L, W):
         o, lse = _decimal_masked(_f(q[0, :, h]), _f(k[0, :, 0]), _f(v[0, :, 0]), scale, visible)
         np.testing.assert_allclose(r["o"][0, :, h], o, rtol=1e-13, atol=1e-14)
         np.testing.assert_allclose(r["lse"][0, h], lse, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Sink logit and the merge of passes over disjoint key sets
+# ("STAGE_D.md — FMHA Kernel Development", D5)
+# --------------------------------------------------------------------------
+
+def test_sink_at_minus_infinity_is_no_sink():
+    q, k, v = _mask_inputs(301, B=2, sq=9, skv=13, hq=4, hkv=2, D=8)
+    for kv_lens in (None, [13, 0]):
+        a = oracle.prefill(q, k, v, scale=0.3, causal=True, dtype="f16", kv_lens=kv_lens)
+        b = oracle.prefill(q, k, v, scale=0.3, causal=True, dtype="f16", kv_lens=kv_lens,
+                           sink_logits=[-np.inf] * 4)
+        for key in ("o", "lse", "row_sum", "row_max", "o_unnorm"):
+            assert a[key].tobytes() == b[key].tobytes(), key
+
+
+@pytest.mark.parametrize("sink,extra", [(0.0, 1), (math.log(3.0), 3), (math.log(0.5), 0.5)])
+def test_sink_tied_scores_closed_form(sink, extra):
+    """q = 0 makes every score 0: row i (causal) sees i + 1 keys of weight 1 and
+    the sink adds exp(sink): LSE = ln(i + 1 + exp(sink)), O = sum of the seen
+    V rows / (i + 1 + exp(sink))."""
+    rng = np.random.default_rng(7)
+    S, D = 6, 4
+    q = np.zeros((1, S, 1, D))
+    k = rng.standard_normal((1, S, 1, D))
+    v = rng.standard_normal((1, S, 1, D))
+    r = oracle.prefill(q, k, v, scale=1.0, causal=True, sink_logits=[sink])
+    for i in range(S):
+        den = i + 1 + extra
+        assert abs(r["lse"][0, 0, i] - math.log(den)) < 1e-14
+        np.testing.assert_allclose(r["o"][0, i, 0], v[0, :i + 1, 0].sum(axis=0) / den,
+                                   rtol=1e-14, atol=1e-15)
+
+
+def test_sink_only_rows():
+    """Rows that see no key keep only the sink: O = 0, LSE = the sink logit,
+    row_max = sink, row_sum = 1."""
+    q, k, v = _mask_inputs(303, B=1, sq=5, skv=7, hq=2, hkv=1, D=4)
+    sinks = [0.75, -2.5]
+    r = oracle.prefill(q, k, v, scale=0.5, causal=True, dtype="f16", kv_lens=[0],
+                       sink_logits=sinks)
+    for h in range(2):
+        assert (r["o"][0, :, h] == 0).all()
+        assert (r["lse"][0, h] == sinks[h]).all() and (r["row_max"][0, h] == sinks[h]).all()
+        assert (r["row_sum"][0, h] == 1.0).all()
+
+
+def _decimal_with_sink(qf, kf, vf, scale, sink):
+    getcontext().prec = 60
+    sc = Decimal(scale)
+    sq = qf.shape[0]
+    out_o = np.zeros((sq, vf.shape[1]))
+    out_lse = np.zeros(sq)
+    off = kf.shape[0] - sq
+    for i in range(sq):
+        js = list(range(i + off + 1))
+        ex = [(sum(Decimal(float(qf[i, d])) * Decimal(float(kf[j, d]))
+                   for d in range(qf.shape[1])) * sc).exp() for j in js]
+        tot = sum(ex) + Decimal(sink).exp()
+        out_lse[i] = float(tot.ln())
+        for d in range(vf.shape[1]):
+            out_o[i, d] = float(sum(e * Decimal(float(vf[j, d])) for j, e in zip(js, ex)) / tot)
+    return out_o, out_lse
+
+
+@pytest.mark.parametrize("sink", [-1.25, 0.5, 3.0])
+def test_sink_brute_force_decimal(sink):
+    sq, skv, D = 4, 6, 3
+    q, k, v = _mask_inputs(311, B=1, sq=sq, skv=skv, hq=2, hkv=1, D=D)
+    scale = float(np.float32(0.6))
+    r = oracle.prefill(q, k, v, scale=scale, causal=True, dtype="f16",
+                       sink_logits=[sink, -sink])
+    for h, sg in ((0, sink), (1, -sink)):
+        o, lse = _decimal_with_sink(_f(q[0, :, h]), _f(k[0, :, 0]), _f(v[0, :, 0]), scale, sg)
+        np.testing.assert_allclose(r["o"][0, :, h], o, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(r["lse"][0, h], lse, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_merge_of_a_key_partition_is_the_whole_pass(seed):
+    """Attention over a key set equals the LSE merge of attention over any
+    partition of it (rows whose part is empty included)."""
+    rng = np.random.default_rng(400 + seed)
+    R, S, D = 7, 19, 5
+    q = rng.standard_normal((R, D))
+    k = rng.standard_normal((S, D)) * 2.0
+    v = rng.standard_normal((S, D))
+    vis = rng.random((R, S)) < 0.7
+    part = rng.random((R, S)) < 0.5
+    part[0] = True                           # row 0: second part empty
+    part[1] = False                          # row 1: first part empty
+    whole = oracle.attend_rows(q, k, v, 0.8, None, vis)
+    a = oracle.attend_rows(q, k, v, 0.8, None, vis & part)
+    b = oracle.attend_rows(q, k, v, 0.8, None, vis & ~part)
+    m = oracle.merge_branches([a["o"], b["o"]], [a["lse"], b["lse"]])
+    np.testing.assert_allclose(m["o"], whole["o"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(m["lse"], whole["lse"], rtol=1e-12, atol=1e-13)
+    # with a sink: the sink is one more branch (O = 0, LSE = sink)
+    ws = oracle.attend_rows(q, k, v, 0.8, None, vis, sink=0.3)
+    m2 = oracle.merge_branches([a["o"], b["o"], np.zeros_like(a["o"])],
+                               [a["lse"], b["lse"], np.full(R, 0.3)])
+    np.testing.assert_allclose(m2["o"], ws["o"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(m2["lse"], ws["lse"], rtol=1e-12, atol=1e-13)
+
+
+def test_merge_branches_large_and_empty():
+    """Weights 1 : 3 at LSE 1000 (no overflow: the merge is max-shifted), and
+    branches with LSE = -inf count for nothing; all-empty gives O = 0, -inf."""
+    o1, o2 = np.array([[1.0, -2.0]]), np.array([[5.0, 2.0]])
+    m = oracle.merge_branches([o1, o2], [np.array([1000.0]), np.array([1000.0 + math.log(3.0)])])
+    np.testing.assert_allclose(m["o"], (o1 + 3 * o2) / 4, rtol=1e-12)  # 1000 + ln 3 rounds
+    assert abs(m["lse"][0] - (1000.0 + math.log(4.0))) < 1e-12
+    m = oracle.merge_branches([o1, o2], [np.array([-np.inf]), np.array([2.5])])
+    assert m["o"].tobytes() == o2.tobytes() and m["lse"][0] == 2.5
+    m = oracle.merge_branches([o1, o2], [np.array([-np.inf]), np.array([-np.inf])])
+    assert (m["o"] == 0).all() and np.isneginf(m["lse"]).all()
