@@ -94,7 +94,9 @@ def _events(torch, n):
     return [_HipEvent(torch) for _ in range(n)]
 
 
-def prefill_setup(torch, fa, cfg):
+def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None):
+    """Prepared (pack, attention) calls for a prefill workload; `tensors`, when
+    a dict, receives the output tensors."""
     from flashattention_attention_amd import inputs
     x = inputs.make_prefill_inputs(cfg)
     q, k, v = (_dev(torch, x[n], cfg.dtype) for n in ("q", "k", "v"))
@@ -111,7 +113,9 @@ def prefill_setup(torch, fa, cfg):
     pack = fa.prefill_pack_v(v, workspace=ws, prepare=True)
     attn = fa.prefill_packed(q, k, ws, causal=cfg.causal, softmax_scale=cfg.scale,
                              out_unnormalized=cfg.out_unnormalized, out=o, lse=lse, row_sum=rs,
-                             window=cfg.window, prepare=True)
+                             window=cfg.window, sink_logits=sink_logits, prepare=True)
+    if tensors is not None:
+        tensors.update(o=o, lse=lse)
 
     def run():
         pack()
@@ -501,6 +505,38 @@ def main():
             "us_per_launch": round(r[1]["mean_ms"] * 1e3, 1),
             "per_launch": f"{wf / 1e12:.4f} TFLOP (visible pairs only)"}
         del w_run, w_pack, w_attn
+        print("[bench] windowed prefill with sinks", file=sys.stderr, flush=True)
+
+        # The same windowed prompt with a per-head sink logit (synthetic values):
+        # folded into the attention epilogue, or merged by a separate in-place
+        # pass over the attention's output.
+        sinks = torch.linspace(-2.0, 6.0, wcfg.n_heads_q, dtype=torch.float32, device="cuda")
+        tens = {}
+        _, s_pack, s_attn = prefill_setup(torch, fa, wcfg, sink_logits=sinks)
+        _, p_pack2, p_attn2 = prefill_setup(torch, fa, wcfg, tensors=tens)
+        s_merge = fa.attn_merge(tens["o"], tens["lse"], sink_logits=sinks, out=tens["o"],
+                                lse=tens["lse"], prepare=True)
+        s_pack(); s_attn(); p_pack2(); p_attn2(); s_merge()
+        rf = time_calls(torch, [s_pack, s_attn], 20)
+        ru = time_calls(torch, [p_pack2, p_attn2, s_merge], 20)
+        fused_ms = rf[0]["mean_ms"] + rf[1]["mean_ms"]
+        unf_ms = ru[0]["mean_ms"] + ru[1]["mean_ms"] + ru[2]["mean_ms"]
+        o_t, l_t = tens["o"], tens["lse"]
+        merge_bytes = 2 * (o_t.numel() + l_t.numel()) * 4 + sinks.numel() * 4
+        merge_gbps = merge_bytes / (ru[2]["mean_ms"] * 1e-3) / 1e9
+        line["prefill_window_sink"] = {
+            "workload": wcfg.name + "_sink", "sinks": "linspace(-2, 6) over the 28 heads",
+            "fused_epilogue_us": round(fused_ms * 1e3, 1),
+            "unfused_us": round(unf_ms * 1e3, 1),
+            "merge_pass_us": round(ru[2]["mean_ms"] * 1e3, 1),
+            "fused_tflops": round(wf / (fused_ms * 1e-3) / 1e12, 2)}
+        rooflines["attn_merge_sink"] = {
+            "bound": "hbm", "achieved": round(merge_gbps, 1), "peak": MI355X_HBM_GBPS,
+            "unit": "GB/s", "frac": round(merge_gbps / MI355X_HBM_GBPS, 4), "traffic": None,
+            "kernel": "branch_merge_kernel<128>",
+            "us_per_launch": round(ru[2]["mean_ms"] * 1e3, 1),
+            "per_launch": f"{merge_bytes / 1e6:.2f} MB (O and LSE read and written once)"}
+        del s_pack, s_attn, p_pack2, p_attn2, s_merge, tens
         del flush_buf
 
     line["roofline"] = rooflines["prefill_gqa_s3314"]

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip", "fa_merge.hip"]
 ARCH = "gfx950"
 
 

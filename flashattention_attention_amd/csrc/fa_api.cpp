@@ -81,10 +81,12 @@ int check_attn(const char* fn, const void* q, int64_t q_sb, int64_t q_ss, int64_
 }
 
 // Length mask and sliding window of a prefill call.
-int check_masks(const char* fn, const int32_t* kv_lens, int window) {
+int check_masks(const char* fn, const int32_t* kv_lens, int window, const float* sink_logits) {
   if (window < 0) return fail(FA_ERR_INVALID_ARG, "%s: window (%d) must be >= 0", fn, window);
   if (kv_lens && ((uintptr_t)kv_lens & 3u))
     return fail(FA_ERR_INVALID_ARG, "%s: kv_lens must be 4-byte aligned", fn);
+  if (sink_logits && ((uintptr_t)sink_logits & 3u))
+    return fail(FA_ERR_INVALID_ARG, "%s: sink_logits must be 4-byte aligned", fn);
   return FA_OK;
 }
 
@@ -115,7 +117,7 @@ fa::PrefillArgs prefill_args(const void* q, int64_t q_sb, int64_t q_ss, int64_t 
                              int64_t o_sb, int64_t o_ss, int64_t o_sh, float* lse,
                              float* row_sum, int batch, int seqlen_q, int seqlen_kv,
                              int n_heads_q, int n_heads_kv, int causal, float softmax_scale,
-                             const int32_t* kv_lens, int window) {
+                             const int32_t* kv_lens, int window, const float* sink_logits) {
   fa::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_sum = row_sum;
   a.q_sb = q_sb; a.q_ss = q_ss; a.q_sh = q_sh;
@@ -128,6 +130,7 @@ fa::PrefillArgs prefill_args(const void* q, int64_t q_sb, int64_t q_ss, int64_t 
   a.scale_log2 = softmax_scale * kLog2e;
   a.kv_lens = kv_lens;
   a.window = window;
+  a.sink_logits = sink_logits;
   return a;
 }
 
@@ -155,12 +158,13 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                    int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                    int head_dim, int dtype, int causal, float softmax_scale,
                    int out_unnormalized, const int32_t* kv_lens, int window,
-                   void* workspace, uint64_t workspace_bytes, void* stream) {
+                   const float* sink_logits, void* workspace, uint64_t workspace_bytes,
+                   void* stream) {
   const char* fn = "fa_prefill_fwd";
   int st = check_attn(fn, q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, o, o_sb, o_ss, o_sh, lse,
                       row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, dtype,
                       softmax_scale, out_unnormalized);
-  if (st == FA_OK) st = check_masks(fn, kv_lens, window);
+  if (st == FA_OK) st = check_masks(fn, kv_lens, window, sink_logits);
   if (st == FA_OK) st = check_pack(fn, v, v_sb, v_ss, v_sh);
   if (st == FA_OK)
     st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
@@ -168,7 +172,7 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
   const fa::PrefillArgs a =
       prefill_args(q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, v, v_sb, v_ss, v_sh, o, o_sb, o_ss,
                    o_sh, lse, row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, causal,
-                   softmax_scale, kv_lens, window);
+                   softmax_scale, kv_lens, window, sink_logits);
   const fa::VtArgs w{workspace, (size_t)workspace_bytes};
   const hipError_t e =
       fa::launch_prefill_pack(a, w, head_dim, dtype == FA_BF16, (hipStream_t)stream);
@@ -207,23 +211,60 @@ int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_s
                           int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                           int head_dim, int dtype, int causal, float softmax_scale,
                           int out_unnormalized, const int32_t* kv_lens, int window,
-                          const void* workspace, uint64_t workspace_bytes, void* stream) {
+                          const float* sink_logits, const void* workspace,
+                          uint64_t workspace_bytes, void* stream) {
   const char* fn = "fa_prefill_fwd_packed";
   int st = check_attn(fn, q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, o, o_sb, o_ss, o_sh, lse,
                       row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, dtype,
                       softmax_scale, out_unnormalized);
-  if (st == FA_OK) st = check_masks(fn, kv_lens, window);
+  if (st == FA_OK) st = check_masks(fn, kv_lens, window, sink_logits);
   if (st == FA_OK)
     st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
   if (st != FA_OK) return st;
   const fa::PrefillArgs a =
       prefill_args(q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, nullptr, 0, 0, 0, o, o_sb, o_ss,
                    o_sh, lse, row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, causal,
-                   softmax_scale, kv_lens, window);
+                   softmax_scale, kv_lens, window, sink_logits);
   const fa::VtArgs w{const_cast<void*>(workspace), (size_t)workspace_bytes};
   return hip_status(fa::launch_prefill_attn(a, w, head_dim, dtype == FA_BF16,
                                             out_unnormalized != 0, (hipStream_t)stream),
                     "fa_prefill_fwd_packed launch");
+}
+
+int fa_attn_merge(const float* o_a, int64_t oa_sb, int64_t oa_ss, int64_t oa_sh,
+                  const float* lse_a, const float* o_b, int64_t ob_sb, int64_t ob_ss,
+                  int64_t ob_sh, const float* lse_b, const float* sink_logits, int batch,
+                  int seqlen, int n_heads, int head_dim, float* o, int64_t o_sb, int64_t o_ss,
+                  int64_t o_sh, float* lse, void* stream) {
+  const char* fn = "fa_attn_merge";
+  if (!o_a || !lse_a || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "%s: o_a, lse_a, o and lse must be non-null", fn);
+  if (!o_b != !lse_b)
+    return fail(FA_ERR_INVALID_ARG, "%s: o_b and lse_b must both be given or both be null", fn);
+  if (batch < 1 || seqlen < 1 || n_heads < 1)
+    return fail(FA_ERR_INVALID_ARG, "%s: batch, seqlen and n_heads must be >= 1", fn);
+  if (!head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+  if (!aligned16(o_a) || !aligned16(o) || (o_b && !aligned16(o_b)))
+    return fail(FA_ERR_INVALID_ARG, "%s: o_a, o_b and o must be 16-byte aligned", fn);
+  if (((uintptr_t)lse_a & 3u) || ((uintptr_t)lse & 3u) || ((uintptr_t)lse_b & 3u) ||
+      ((uintptr_t)sink_logits & 3u))
+    return fail(FA_ERR_INVALID_ARG, "%s: lse and sink arrays must be 4-byte aligned", fn);
+  const int64_t st[9] = {oa_sb, oa_ss, oa_sh, ob_sb, ob_ss, ob_sh, o_sb, o_ss, o_sh};
+  for (int i = 0; i < 9; ++i)
+    if ((i < 3 || i >= 6 || o_b) && (st[i] < 0 || st[i] % 4))
+      return fail(FA_ERR_INVALID_ARG, "%s: o strides must be non-negative multiples of 4", fn);
+  if ((int64_t)batch * seqlen * n_heads * (head_dim / 4) > ((int64_t)1 << 40))
+    return fail(FA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  fa::BranchMergeArgs a;
+  a.o_a = o_a; a.lse_a = lse_a; a.o_b = o_b; a.lse_b = lse_b; a.sink_logits = sink_logits;
+  a.o = o; a.lse = lse;
+  a.oa_sb = oa_sb; a.oa_ss = oa_ss; a.oa_sh = oa_sh;
+  a.ob_sb = ob_sb; a.ob_ss = ob_ss; a.ob_sh = ob_sh;
+  a.o_sb = o_sb; a.o_ss = o_ss; a.o_sh = o_sh;
+  a.batch = batch; a.seqlen = seqlen; a.n_heads = n_heads;
+  return hip_status(fa::launch_branch_merge(a, head_dim, (hipStream_t)stream),
+                    "fa_attn_merge launch");
 }
 
 uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int head_dim) {

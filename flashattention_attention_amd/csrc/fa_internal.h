@@ -23,6 +23,7 @@ struct PrefillArgs {
   float scale_log2;        // softmax_scale * log2(e)
   const int32_t* kv_lens;  // device [batch] valid KV length per sequence, or null
   int window;              // > 0: key j visible only if j > q_pos - window
+  const float* sink_logits;  // device [n_heads_q] per-head sink logit, or null
 };
 
 struct DecodeArgs {
@@ -45,6 +46,19 @@ struct DecodeArgs {
   float* wg_o;       // [batch, n_heads_q, max_wg, head_dim]
   float* wg_lse;     // [batch, n_heads_q, max_wg]
   int max_wg;        // work-groups per (sequence, head group)
+};
+
+// Merge of two attention passes (and an optional per-head sink) by LSE.
+struct BranchMergeArgs {
+  const float* o_a;
+  const float* lse_a;
+  const float* o_b;          // may be null (no second pass)
+  const float* lse_b;
+  const float* sink_logits;  // may be null
+  float* o;
+  float* lse;
+  int64_t oa_sb, oa_ss, oa_sh, ob_sb, ob_ss, ob_sh, o_sb, o_ss, o_sh;
+  int batch, seqlen, n_heads;
 };
 
 struct MergeArgs {
@@ -76,6 +90,7 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                                  hipStream_t stream);
 hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_branch_merge(const BranchMergeArgs& a, int head_dim, hipStream_t stream);
 
 // Splits (one per wave) merged inside one work-group of the single-launch decode.
 int decode_fused_waves(int head_dim, int max_splits);

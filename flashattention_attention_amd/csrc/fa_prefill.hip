@@ -73,6 +73,7 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 constexpr float kShift = 7.0f;            // log2 of the fp16 headroom factor on P
 constexpr float kSlack = 8.0f;            // stale-max tolerance (log2 units)
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.44269504088896341f;
 
 // Work-group geometry per head dim. key_split(d) = 1: every wave owns its own
 // 32 query rows and takes whole 64-key tiles. key_split(d) = 2 (head_dim 256,
@@ -613,13 +614,32 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   }
 
   // Refer the outputs back to the true row max: factor = 2^((m_used - kShift) - m_true).
-  const float to_true = exp2_fast(m_used - kShift - m_true);
-  // a row with no visible key (length or window mask) has lt = 0: O = 0, LSE = -inf
-  const float f = UNNORM ? to_true : (lt > 0.0f ? 1.0f / lt : 0.0f);
+  const float base = m_used - kShift;    // the exponentials (and lt) are relative to 2^base
+  float f, lse2, rsum;
+  if (!a.sink_logits) {
+    const float to_true = exp2_fast(base - m_true);
+    // a row with no visible key (length or window mask) has lt = 0: O = 0, LSE = -inf
+    f = UNNORM ? to_true : (lt > 0.0f ? 1.0f / lt : 0.0f);
+    lse2 = base + __log2f(lt);
+    rsum = lt * to_true;
+  } else {
+    // The sink joins the softmax as one more term 2^sg with no value row. The
+    // output's reference max becomes max(m_true, sg); in normalized form the
+    // factor is 2^(base - LSE), all in log2 units, so nothing overflows.
+    const float sg = a.sink_logits[h] * kLog2e;
+    const float lns = lt > 0.0f ? base + __log2f(lt) : -INFINITY;   // log2 of the key terms
+    const float mx = fmaxf(lns, sg);
+    lse2 = mx == -INFINITY ? -INFINITY   // no key and a sink at -inf
+                           : mx + __log2f(exp2_fast(lns - mx) + exp2_fast(sg - mx));
+    const float mr = fmaxf(m_true, sg);
+    const float to_ref = lt > 0.0f ? exp2_fast(base - mr) : 0.0f;
+    f = UNNORM ? to_ref : (lt > 0.0f ? exp2_fast(base - lse2) : 0.0f);
+    rsum = lt * to_ref + exp2_fast(sg - mr);
+  }
   if (hh == 0 && q_valid) {
     const int64_t ri = ((int64_t)b * a.n_heads_q + h) * a.seqlen_q + qi;
-    a.lse[ri] = (m_used - kShift + __log2f(lt)) * kLn2;
-    if (a.row_sum) a.row_sum[ri] = lt * to_true;
+    a.lse[ri] = lse2 * kLn2;
+    if (a.row_sum) a.row_sum[ri] = rsum;
   }
 
   // Stage this wave's 32 output rows in LDS ([row][D] fp32, 16-byte chunks

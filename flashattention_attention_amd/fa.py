@@ -29,13 +29,15 @@ _SIGNATURES = {
     "fa_prefill_fwd": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                         _vp, _i64, _i64, _i64, _vp, _vp,
                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
-                        _vp, _i32, _vp, ctypes.c_uint64, _vp], _i32),
+                        _vp, _i32, _vp, _vp, ctypes.c_uint64, _vp], _i32),
     "fa_prefill_pack_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                            _vp, ctypes.c_uint64, _vp], _i32),
     "fa_prefill_fwd_packed": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                _vp, _i64, _i64, _i64, _vp, _vp,
                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
-                               _vp, _i32, _vp, ctypes.c_uint64, _vp], _i32),
+                               _vp, _i32, _vp, _vp, ctypes.c_uint64, _vp], _i32),
+    "fa_attn_merge": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
+                       _i32, _i32, _i32, _i32, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "fa_prefill_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
     "fa_decode_plan": ([ctypes.POINTER(ctypes.c_int32), _i32, _i32, _i32, _i32, _i32,
                         ctypes.POINTER(_i32), ctypes.POINTER(_i32)], _i32),
@@ -183,6 +185,23 @@ def _masks(kv_lens, window, batch, dev):
     return kv_lens, window
 
 
+def _sinks(sink_logits, n_heads, dev):
+    """Check the optional per-head sink logits (fp32 GPU tensor [n_heads])."""
+    if sink_logits is None:
+        return None
+    _on_gpu(sink_logits)
+    if sink_logits.device != dev:
+        raise FAError("sink_logits must be on the same GPU as the other tensors")
+    if sink_logits.dtype != torch.float32 or sink_logits.shape != (n_heads,) \
+            or not sink_logits.is_contiguous():
+        raise FAError("sink_logits must be a contiguous fp32 tensor [n_heads]")
+    return sink_logits
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
 def _workspace(k, dev, workspace):
     B, Skv, Hkv, D = k.shape
     ws_need = load_library().fa_prefill_workspace_size(B, Skv, Hkv, D)
@@ -199,13 +218,14 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
             row_sum: Optional[torch.Tensor] = None, want_row_sum: bool = False,
             workspace: Optional[torch.Tensor] = None, kv_lens: Optional[torch.Tensor] = None,
-            window: int = 0):
+            window: int = 0, sink_logits: Optional[torch.Tensor] = None):
     """Attention forward. q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (fp16/bf16, D contiguous).
 
     ``kv_lens`` (optional int32 GPU tensor [B]) hides keys j >= kv_lens[b];
     ``window`` > 0 hides keys j <= p - window for the query at position p
     (p = row + Skv - Sq). Rows that see no key come back with o = 0,
-    lse = -inf.
+    lse = -inf. ``sink_logits`` (optional fp32 GPU tensor [Hq]) adds a per-head
+    sink term exp(sink) with no value row to every row's softmax.
 
     ``workspace`` (optional) is a uint8 GPU tensor of at least
     ``prefill_workspace_size(...)`` bytes; one is allocated when omitted.
@@ -225,6 +245,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
     Skv, Hkv = k.shape[1], k.shape[2]
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
     kv_lens, window = _masks(kv_lens, window, B, dev)
+    sink_logits = _sinks(sink_logits, Hq, dev)
     workspace = _workspace(k, dev, workspace)
     st = load_library().fa_prefill_fwd(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
@@ -233,9 +254,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
         B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
-        1 if out_unnormalized else 0, kv_lens.data_ptr() if kv_lens is not None else None,
-        window, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _stream(dev))
+        1 if out_unnormalized else 0, _ptr(kv_lens), window, _ptr(sink_logits),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st, "fa_prefill_fwd")
     return (out, lse, row_sum) if need_rs else (out, lse)
 
@@ -261,7 +281,8 @@ def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
                    out_unnormalized: bool = False, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, row_sum: Optional[torch.Tensor] = None,
                    want_row_sum: bool = False, kv_lens: Optional[torch.Tensor] = None,
-                   window: int = 0, prepare: bool = False):
+                   window: int = 0, sink_logits: Optional[torch.Tensor] = None,
+                   prepare: bool = False):
     """prefill() with V taken from a workspace filled by prefill_pack_v (same shapes).
     With prepare=True, returns a callable that repeats the call (pass the outputs)."""
     dev = _on_gpu(q, k, packed_v)
@@ -271,18 +292,69 @@ def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
     Skv, Hkv = k.shape[1], k.shape[2]
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
     kv_lens, window = _masks(kv_lens, window, B, dev)
+    sink_logits = _sinks(sink_logits, Hq, dev)
     call = _issue("fa_prefill_fwd_packed", (
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
         B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
-        1 if out_unnormalized else 0, kv_lens.data_ptr() if kv_lens is not None else None,
-        window, packed_v.data_ptr(), packed_v.numel() * packed_v.element_size(), _stream(dev)),
-        (q, k, packed_v, out, lse, row_sum, kv_lens), prepare)
+        1 if out_unnormalized else 0, _ptr(kv_lens), window, _ptr(sink_logits),
+        packed_v.data_ptr(), packed_v.numel() * packed_v.element_size(), _stream(dev)),
+        (q, k, packed_v, out, lse, row_sum, kv_lens, sink_logits), prepare)
     if prepare:
         return call
     return (out, lse, row_sum) if need_rs else (out, lse)
+
+
+def attn_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: Optional[torch.Tensor] = None,
+               lse_b: Optional[torch.Tensor] = None, *,
+               sink_logits: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, prepare: bool = False):
+    """Merge two attention passes (and/or a per-head sink) by LSE.
+
+    o_a, o_b: fp32 [B,S,H,D] (D contiguous; decode outputs [B,H,D] count as
+    S = 1), lse_a, lse_b: fp32 [B,H,S] (or [B,H]); sink_logits fp32 [H].
+    ``out``/``lse`` may be o_a/lse_a (in place). Returns (o, lse), or with
+    prepare=True a callable that repeats the call."""
+    squeeze = o_a.dim() == 3
+    if squeeze:                                  # decode layout: one query per sequence
+        o_a, lse_a = o_a.unsqueeze(1), lse_a.unsqueeze(2)
+        o_b = o_b.unsqueeze(1) if o_b is not None else None
+        lse_b = lse_b.unsqueeze(2) if lse_b is not None else None
+        out = out.unsqueeze(1) if out is not None else None
+        lse = lse.unsqueeze(2) if lse is not None else None
+    if (o_b is None) != (lse_b is None):
+        raise FAError("o_b and lse_b go together")
+    dev = _on_gpu(o_a, lse_a, *[t for t in (o_b, lse_b) if t is not None])
+    if o_a.dim() != 4:
+        raise FAError("o_a must be [B,S,H,D] or [B,H,D]")
+    B, S, H, D = o_a.shape
+    for t in (o_a, o_b):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, S, H, D)
+                              or t.stride(3) != 1):
+            raise FAError("o_a / o_b must be fp32 of one shape with contiguous head_dim")
+    for t in (lse_a, lse_b):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, S)
+                              or not t.is_contiguous()):
+            raise FAError("lse_a / lse_b must be contiguous fp32 [B,H,S]")
+    sink_logits = _sinks(sink_logits, H, dev)
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    _on_gpu(out, lse)
+    if out.dtype != torch.float32 or out.shape != (B, S, H, D) or out.stride(3) != 1 \
+            or lse.dtype != torch.float32 or lse.shape != (B, H, S) or not lse.is_contiguous():
+        raise FAError("out / lse have the wrong shape, dtype or layout")
+    ob_st = o_b.stride()[:3] if o_b is not None else (0, 0, 0)
+    call = _issue("fa_attn_merge", (
+        o_a.data_ptr(), *o_a.stride()[:3], lse_a.data_ptr(), _ptr(o_b), *ob_st, _ptr(lse_b),
+        _ptr(sink_logits), B, S, H, D, out.data_ptr(), *out.stride()[:3], lse.data_ptr(),
+        _stream(dev)), (o_a, lse_a, o_b, lse_b, sink_logits, out, lse), prepare)
+    if prepare:
+        return call
+    return (out.squeeze(1), lse.squeeze(2)) if squeeze else (out, lse)
 
 
 def prefill_workspace_size(batch: int, seqlen_kv: int, n_heads_kv: int, head_dim: int) -> int:

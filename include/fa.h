@@ -81,7 +81,15 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  * device. window == 0 disables the window; window < 0 is rejected. The masks
  * combine freely (causal == 0 with a window admits every key after
  * p_i - window). A row that sees no key gets o = 0, row_sum = 0 and
- * lse = -inf. Hidden keys that share a 64-key tile with visible ones are read
+ * lse = -inf.
+ *
+ * sink_logits: DEVICE array [n_heads_q] of fp32 (4-byte aligned) or NULL. The
+ * sink of query head h joins every row's softmax as one more term
+ * exp(sink_logits[h]) with no value row (D5/D5d: the sink merge folded into
+ * the epilogue), so lse = ln(sum_j exp(s_ij) + exp(sink)), o is normalized by
+ * that sum, and in un-normalized mode o and row_sum refer to
+ * m_i = max(max_j s_ij, sink). A row with no key then gets o = 0,
+ * lse = sink (row_sum = 1 in un-normalized mode). Hidden keys that share a 64-key tile with visible ones are read
  * and given weight zero, so K and V must hold finite values there too (V
  * within fp16 range; padding past kv_lens[b] included); tiles with no visible
  * key are skipped.
@@ -114,7 +122,8 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                    int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                    int head_dim, int dtype, int causal, float softmax_scale,
                    int out_unnormalized, const int32_t* kv_lens, int window,
-                   void* workspace, uint64_t workspace_bytes, void* stream);
+                   const float* sink_logits, void* workspace, uint64_t workspace_bytes,
+                   void* stream);
 
 /*
  * fa_prefill_pack_v / fa_prefill_fwd_packed — fa_prefill_fwd in its two
@@ -147,7 +156,35 @@ int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_s
                           int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                           int head_dim, int dtype, int causal, float softmax_scale,
                           int out_unnormalized, const int32_t* kv_lens, int window,
-                          const void* workspace, uint64_t workspace_bytes, void* stream);
+                          const float* sink_logits, const void* workspace,
+                          uint64_t workspace_bytes, void* stream);
+
+/*
+ * fa_attn_merge — merge two attention passes over disjoint key sets, and an
+ * optional per-head sink, through their LSEs.
+ *
+ * Source: "STAGE_D.md — FMHA Kernel Development", D5 (a sliding-window pass
+ * and a sink merged by LSE; D5b does it after the kernels, as here). The
+ * formula is not printed on the pages; the max-shifted form is used, with the
+ * sink as a pass whose O is 0 and whose LSE is sink_logits[h]:
+ *   M = max(lse_a, lse_b, sink), w_x = exp(lse_x - M),
+ *   o = (w_a o_a + w_b o_b) / (w_a + w_b + w_sink), lse = M + ln(w_a + w_b + w_sink);
+ * rows where every term is -inf get o = 0, lse = -inf. For passes over
+ * disjoint key sets this is the attention over their union.
+ *
+ * Layouts (fp32, element strides, head_dim contiguous): o_a, o_b, o
+ * [batch, seqlen, n_heads, head_dim] (16-byte aligned, strides multiples of
+ * 4); lse_a, lse_b, lse [batch, n_heads, seqlen] contiguous (the layout
+ * fa_prefill_fwd writes; decode outputs are the case seqlen = 1);
+ * sink_logits [n_heads]. o_b and lse_b may both be NULL (one pass, e.g. with
+ * a sink), sink_logits may be NULL. o may be o_a and lse may be lse_a (in
+ * place); no other overlap is allowed. All device memory.
+ */
+int fa_attn_merge(const float* o_a, int64_t oa_sb, int64_t oa_ss, int64_t oa_sh,
+                  const float* lse_a, const float* o_b, int64_t ob_sb, int64_t ob_ss,
+                  int64_t ob_sh, const float* lse_b, const float* sink_logits, int batch,
+                  int seqlen, int n_heads, int head_dim, float* o, int64_t o_sb, int64_t o_ss,
+                  int64_t o_sh, float* lse, void* stream);
 
 /*
  * fa_prefill_workspace_size — bytes of workspace fa_prefill_fwd needs

@@ -26,6 +26,7 @@ def test_exports_every_declared_symbol():
                           "fa_prefill_workspace_size", "fa_decode_plan",
                           "fa_decode_split_partial", "fa_decode_merge_lse", "fa_decode_fused",
                           "fa_decode_fused_workspace_size", "fa_decode_fused_waves",
+                          "fa_attn_merge",
                           "fa_status_string", "fa_last_error"}
     lib = ctypes.CDLL(fa.library_path())
     for name in names:
@@ -84,15 +85,16 @@ def _prefill(**kw):
     base = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED, row_sum=None,
                 B=1, Sq=128, Skv=128, Hq=4, Hkv=2, D=128, dtype=0, causal=1, scale=0.125,
                 unnorm=0, qs=(128 * 4 * 128, 4 * 128, 128), ks=(128 * 2 * 128, 2 * 128, 128),
-                os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40, lens=None, win=0)
+                os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40, lens=None, win=0,
+                sink=None)
     base.update(kw)
     b = base
     lib = fa.load_library()
     return lib.fa_prefill_fwd(b["q"], *b["qs"], b["k"], *b["ks"], b["v"], *b["ks"],
                               b["o"], *b["os"], b["lse"], b["row_sum"], b["B"], b["Sq"],
                               b["Skv"], b["Hq"], b["Hkv"], b["D"], b["dtype"], b["causal"],
-                              b["scale"], b["unnorm"], b["lens"], b["win"], b["ws"], b["wsb"],
-                              None)
+                              b["scale"], b["unnorm"], b["lens"], b["win"], b["sink"], b["ws"],
+                              b["wsb"], None)
 
 
 @pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
@@ -105,7 +107,7 @@ def _prefill(**kw):
     (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1), (dict(os=(128, 2, 128)), 1),
     (dict(ks=(-8, 256, 128)), 1), (dict(Sq=2**31 - 1, Skv=2**31 - 1, Hq=128), 2),
     (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(ws=ALIGNED + 16), 1),
-    (dict(win=-1), 1), (dict(lens=ALIGNED + 2), 1),
+    (dict(win=-1), 1), (dict(lens=ALIGNED + 2), 1), (dict(sink=ALIGNED + 2), 1),
 ])
 def test_prefill_validation(kw, status):
     st = _prefill(**kw)
@@ -140,13 +142,15 @@ def test_prefill_fwd_packed_validation(kw, status):
     b = dict(q=ALIGNED, k=ALIGNED, o=ALIGNED, lse=ALIGNED, row_sum=None, B=1, Sq=128, Skv=128,
              Hq=4, Hkv=2, D=128, dtype=0, causal=1, scale=0.125, unnorm=0,
              qs=(128 * 4 * 128, 4 * 128, 128), ks=(128 * 2 * 128, 2 * 128, 128),
-             os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40, lens=None, win=0)
+             os=(128 * 4 * 128, 4 * 128, 128), ws=ALIGNED, wsb=1 << 40, lens=None, win=0,
+             sink=None)
     b.update(kw)
     lib = fa.load_library()
     st = lib.fa_prefill_fwd_packed(b["q"], *b["qs"], b["k"], *b["ks"], b["o"], *b["os"],
                                    b["lse"], b["row_sum"], b["B"], b["Sq"], b["Skv"], b["Hq"],
                                    b["Hkv"], b["D"], b["dtype"], b["causal"], b["scale"],
-                                   b["unnorm"], b["lens"], b["win"], b["ws"], b["wsb"], None)
+                                   b["unnorm"], b["lens"], b["win"], b["sink"], b["ws"],
+                                   b["wsb"], None)
     assert st == status, lib.fa_last_error()
 
 
@@ -218,6 +222,24 @@ def test_decode_fused_workspace_size():
     assert lib.fa_decode_fused_workspace_size(32, 32, 8, 128, 13) == want
     assert lib.fa_decode_fused_workspace_size(1, 4, 3, 128, 4) == 0
     assert lib.fa_decode_fused_workspace_size(1, 4, 2, 96, 4) == 0
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
+@pytest.mark.parametrize("kw,status", [
+    (dict(oa=None), 1), (dict(la=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
+    (dict(ob=ALIGNED, lb=None), 1), (dict(ob=None, lb=ALIGNED), 1), (dict(B=0), 1),
+    (dict(D=96), 2), (dict(oa=ALIGNED + 4), 1), (dict(sink=ALIGNED + 1), 1),
+    (dict(oas=(512, 128, 130)), 1), (dict(os_=(-4, 128, 128)), 1),
+])
+def test_attn_merge_validation(kw, status):
+    b = dict(oa=ALIGNED, oas=(512 * 4, 512, 128), la=ALIGNED, ob=ALIGNED, obs=(512 * 4, 512, 128),
+             lb=ALIGNED, sink=None, B=1, S=4, H=4, D=128, o=ALIGNED, os_=(512 * 4, 512, 128),
+             lse=ALIGNED)
+    b.update(kw)
+    lib = fa.load_library()
+    st = lib.fa_attn_merge(b["oa"], *b["oas"], b["la"], b["ob"], *b["obs"], b["lb"], b["sink"],
+                           b["B"], b["S"], b["H"], b["D"], b["o"], *b["os_"], b["lse"], None)
+    assert st == status, lib.fa_last_error()
 
 
 def test_workspace_size():
