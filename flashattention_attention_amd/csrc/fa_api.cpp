@@ -30,6 +30,7 @@ int ok() {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool head_dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
+bool prefill_head_dim_supported(int d) { return head_dim_supported(d) || d == 512; }
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -57,8 +58,8 @@ int check_attn(const char* fn, const void* q, int64_t q_sb, int64_t q_ss, int64_
   if (n_heads_q % n_heads_kv != 0)
     return fail(FA_ERR_INVALID_ARG, "%s: n_heads_q (%d) %% n_heads_kv (%d) != 0", fn, n_heads_q,
                 n_heads_kv);
-  if (!head_dim_supported(head_dim))
-    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+  if (!prefill_head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256, 512}", fn, head_dim);
   if (dtype != FA_F16 && dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F16 or FA_BF16", fn, dtype);
   if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
@@ -188,8 +189,8 @@ int fa_prefill_pack_v(const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh, i
   const char* fn = "fa_prefill_pack_v";
   if (batch < 1 || seqlen_kv < 1 || n_heads_kv < 1)
     return fail(FA_ERR_INVALID_ARG, "%s: batch, seqlen_kv and n_heads_kv must be >= 1", fn);
-  if (!head_dim_supported(head_dim))
-    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+  if (!prefill_head_dim_supported(head_dim))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256, 512}", fn, head_dim);
   if (dtype != FA_F16 && dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F16 or FA_BF16", fn, dtype);
   int st = check_pack(fn, v, v_sb, v_ss, v_sh);

@@ -3,7 +3,8 @@
 // Two launches on the caller's stream:
 //
 //  1. vt_pack_kernel: V [B, Skv, Hkv, D] (fp16 or bf16) -> fp16 V^T tiles in
-//     the caller's workspace, laid out [B][Hkv][tile][D][64 keys], keys in
+//     the caller's workspace, laid out [B][Hkv][tile][D][T keys] (T = 64;
+//     32 at head_dim 512), keys in
 //     the order the P.V
 //     contraction consumes them, 16-byte chunks XOR-swizzled inside every
 //     row, and zero-filled keys past Skv. bf16 V is converted to fp16 here, once, instead of in every
@@ -16,7 +17,8 @@
 //     two work-groups share a compute unit. At head_dim 256 a work-group has
 //     8 waves: waves w and w+4 own the same 32 rows (128 per block), each
 //     takes half of every tile with its own online softmax, and the pair is
-//     merged at the end.
+//     merged at the end. Head_dim 512 has its own kernel (prefill512_kernel)
+//     in which the two waves of a pair split the head dimension instead.
 //
 // Mapping to the CDNA4 matrix cores (v_mfma_f32_32x32x16_{bf16,f16}): each
 // wave computes the TRANSPOSED score tile S^T = K . Q^T (keys along M, its 32
@@ -89,7 +91,7 @@ __host__ __device__ constexpr int key_split(int d) { return d <= 128 ? 1 : 2; }
 // 8 at head_dim 256 (four wave pairs).
 __host__ __device__ constexpr int wg_waves(int d, int hp) { return d <= 128 ? 4 * hp : 8; }
 __host__ __device__ constexpr int tile_keys(int d) {
-  return key_split(d) == 1 ? 64 : (d <= 128 ? 128 : 64);
+  return d == 512 ? 32 : (key_split(d) == 1 ? 64 : (d <= 128 ? 128 : 64));
 }
 __host__ __device__ constexpr int block_rows(int d) { return 128; }
 
@@ -156,7 +158,8 @@ __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" :
 template <int BN>
 __device__ __forceinline__ int vt_chunk_offset(int d, int c) {
   if constexpr (BN == 128) return d * 256 + ((c ^ (d & 15)) << 4);
-  else return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
+  else if constexpr (BN == 64) return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
+  else return d * 64 + ((c ^ ((d >> 2) & 3)) << 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -669,6 +672,242 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Attention forward at head_dim 512 ("STAGE_D.md — FMHA Kernel Development",
+// D1.4: a 512-wide head overflows the on-chip budget that fits the narrower
+// heads; of the page's options this kernel splits the contraction dimension
+// of Q.K^T). A wave cannot hold 32 query rows of Q and of the fp32 output at
+// 512 dims in its 256 registers, so the two waves of a pair split the head
+// dimension: each holds Q and O for 256 dims and computes the partial S^T
+// over them, the pair adds the two partials through LDS (a + b = b + a in
+// fp32, so both waves hold bitwise the same S), both run the same online
+// softmax, and each multiplies P into its half of V. 8 waves = 4 query groups
+// of 32 rows x 2 halves; 32-key tiles; LDS: two stages of K (32 KB) and V^T
+// (32 KB) plus 32 KB of partial scores, the 160 KB of a compute unit.
+// ---------------------------------------------------------------------------
+template <bool BF16, bool UNNORM>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
+  constexpr int D = 512, DH = 256;           // head dim; dims per wave
+  constexpr int QG = 4;                      // query groups of 32 rows
+  constexpr int kBM = 32 * QG;               // query rows per work-group
+  constexpr int BN = tile_keys(D);           // keys per tile
+  static_assert(BN == 32, "one 32-key MFMA block per tile");
+  constexpr int NKK = DH / 16;               // MFMA k-steps of the partial Q.K^T
+  constexpr int NDB = DH / 32;               // 32-row blocks of this wave's O^T
+  constexpr int NKS = BN / 16;               // MFMA k-steps of P.V
+  constexpr int KROW = D * 2;                // bytes per K row (one DMA instruction)
+  constexpr int KT = BN * KROW;
+  constexpr int VT = D * BN * 2;
+  constexpr int STAGE = KT + VT;
+  constexpr int K_INSTR = BN / 8;            // K rows per wave per tile
+  constexpr int V_INSTR = VT / 1024 / 8;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE + 8 * 16 * 64 * 4];
+  float* xch = (float*)(lds + 2 * STAGE);    // [wave][element][lane] partial S^T
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qw = wave % QG;                  // which 32 query rows
+  const int dh = wave / QG;                  // which half of the head dims
+  const int nqb = (a.seqlen_q + kBM - 1) / kBM;
+  const int per_group = a.n_heads_q / a.n_heads_kv;
+  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group, nqb);
+  if (!item.valid) return;
+  const int qb = item.qb, b = item.b, hk = item.hk;
+  const int h = hk * per_group + item.unit;
+  const int q0 = qb * kBM;
+  const int off = a.seqlen_kv - a.seqlen_q;  // bottom-right alignment
+
+  const int n = lane & 31;    // MFMA column = this lane's query within the wave
+  const int hh = lane >> 5;   // lane half
+  const int qi = q0 + qw * 32 + n;
+  const bool q_valid = qi < a.seqlen_q;
+  const int qpos = qi + off;
+
+  u32x4 qr[NKK];              // Q^T operand: this lane's query, this wave's dims
+  auto load_q = [&]() {
+    const unsigned short* qp = (const unsigned short*)a.q + (int64_t)b * a.q_sb +
+                               (int64_t)qi * a.q_ss + (int64_t)h * a.q_sh + dh * DH;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qr[kk] = q_valid ? *(const u32x4*)(qp + kk * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qr[kk]));
+  };
+
+  // Keys this work-group may see, as in prefill_kernel: [kv_lo, kv_end).
+  const int kv_len = a.kv_lens ? min(max(a.kv_lens[b], 0), a.seqlen_kv) : a.seqlen_kv;
+  int kv_end = kv_len;
+  if (a.causal) kv_end = min(kv_end, min(q0 + kBM, a.seqlen_q) + off);
+  const int kv_lo = a.window > 0 ? max(0, q0 + off - a.window + 1) : 0;
+  const int tb = kv_lo / BN;
+  const int ntiles = kv_end > kv_lo ? (kv_end + BN - 1) / BN - tb : 0;
+  const int ntiles_all = (a.seqlen_kv + BN - 1) / BN;
+  const int wave_first_qpos = q0 + qw * 32 + off;
+
+  const unsigned short* kp =
+      (const unsigned short*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
+  const char* vtp = (const char*)vt_ws + ((int64_t)b * a.n_heads_kv + hk) * ntiles_all * VT;
+  const unsigned lds_base = (unsigned)(uintptr_t)(lptr_t)lds;
+
+  // DMA of tile tb + t into the stage at LDS offset st. K: one 1 KB row per
+  // instruction; lane p stores the row's 16-byte chunk p ^ (row & 15) at
+  // position p (the swizzle that spreads an operand load over the banks).
+  auto issue = [&](int t, unsigned st) {
+    const int t0 = (tb + t) * BN;
+#pragma unroll
+    for (int j = 0; j < K_INSTR; ++j) {
+      const int r = wave * K_INSTR + j;
+      const int key = min(t0 + r, a.seqlen_kv - 1);   // rows past the end: masked below
+      dma16(kp + (int64_t)key * a.k_ss + ((lane ^ (r & 15)) << 3), lds_base + st + r * KROW);
+    }
+#pragma unroll
+    for (int j = 0; j < V_INSTR; ++j) {
+      const int J = wave * V_INSTR + j;
+      dma16(vtp + (int64_t)(tb + t) * VT + J * 1024 + lane * 16, lds_base + st + KT + J * 1024);
+    }
+  };
+
+  // Operand offsets: K row n, logical chunk dh*32 + 2*kk + hh (the XOR only
+  // touches the low 4 bits of the chunk index, so it is split off per kk % 8).
+  int ka8[8];
+#pragma unroll
+  for (int k8 = 0; k8 < 8; ++k8) ka8[k8] = n * KROW + (((2 * k8 + hh) ^ (n & 15)) << 4);
+  int va_off[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) va_off[ks] = dh * DH * (BN * 2) + vt_chunk_offset<BN>(n, 2 * ks + hh);
+
+  float m_used = -1e30f, m_true = -1e30f, l = 0.0f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+
+  auto qk = [&](const char* kst, f32x16& s) {
+    s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      s = mfma_qk<BF16>(*(const u32x4*)(kst + ka8[kk % 8] + (dh * 32 + (kk / 8) * 16) * 16),
+                        qr[kk], s);
+  };
+  // Mask, row max and (rarely) the move of the exponent base, as in prefill_kernel.
+  auto prep = [&](f32x16& s, int t0) -> float {
+    const bool need_mask = (a.causal && t0 + BN - 1 > wave_first_qpos) || (t0 + BN > kv_len) ||
+                           (a.window > 0 && t0 <= wave_first_qpos + 31 - a.window);
+    if (need_mask) {
+      const int hi = min(a.causal ? qpos : INT_MAX, kv_len - 1) - t0 - hh * 4;
+      const int lo = a.window > 0 ? qpos - a.window + 1 - t0 - hh * 4 : INT_MIN;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = (i >> 2) * 8 + (i & 3);
+        if (j > hi || j < lo) s[i] = -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = max_halves(mx);
+    const float tmax = mx * a.scale_log2;
+    m_true = fmaxf(m_true, tmax);
+    const bool grow = tmax > m_used + kSlack;
+    if (__ballot(grow)) {
+      const float nm = grow ? tmax : m_used;
+      const float corr = exp2_fast(m_used - nm);
+      m_used = nm;
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+    }
+    return m_used - kShift;
+  };
+  auto expo = [&](const f32x16& s, float base, u32x4 (&pk)[NKS]) {
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = exp2_fast(__builtin_fmaf(s[i], a.scale_log2, -base));
+      const float p1 = exp2_fast(__builtin_fmaf(s[i + 1], a.scale_log2, -base));
+      ls[(i >> 1) & 3] += p0 + p1;
+      pk[i >> 3][(i & 7) >> 1] = pack_f16x2(p0, p1);
+    }
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  auto pv = [&](const char* vst, const u32x4 (&pk)[NKS]) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma_pv(*(const u32x4*)(vst + va_off[ks] + db * 32 * (BN * 2)), pk[ks],
+                           oacc[db]);
+  };
+
+  // Plain double buffer: tile t+1 arrives while tile t is computed. Two
+  // barriers per tile: one publishes the partial scores, one publishes tile
+  // t+1 and frees tile t's stage (and the score area).
+  constexpr unsigned ST_[2] = {0, STAGE};
+  auto step = [&](int t, auto stage) {
+    constexpr int ST = decltype(stage)::value;
+    if (t + 1 < ntiles) issue(t + 1, ST_[1 - ST]);
+    f32x16 s;
+    qk(lds + ST_[ST], s);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xch[(wave * 16 + i) * 64 + lane] = s[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] += xch[((wave ^ 4) * 16 + i) * 64 + lane];
+    const float base = prep(s, (tb + t) * BN);
+    u32x4 pk[NKS];
+    expo(s, base, pk);
+    pv(lds + ST_[ST] + KT, pk);
+    dma_wait();
+    __syncthreads();
+  };
+  if (ntiles > 0) issue(0, ST_[0]);
+  load_q();
+  dma_wait();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  const float lt = sum_halves(l);
+  const float base = m_used - kShift;
+  float f, lse2, rsum;
+  if (!a.sink_logits) {
+    const float to_true = exp2_fast(base - m_true);
+    f = UNNORM ? to_true : (lt > 0.0f ? 1.0f / lt : 0.0f);
+    lse2 = base + __log2f(lt);
+    rsum = lt * to_true;
+  } else {
+    const float sg = a.sink_logits[h] * kLog2e;
+    const float lns = lt > 0.0f ? base + __log2f(lt) : -INFINITY;
+    const float mx = fmaxf(lns, sg);
+    lse2 = mx == -INFINITY ? -INFINITY
+                           : mx + __log2f(exp2_fast(lns - mx) + exp2_fast(sg - mx));
+    const float mr = fmaxf(m_true, sg);
+    const float to_ref = lt > 0.0f ? exp2_fast(base - mr) : 0.0f;
+    f = UNNORM ? to_ref : (lt > 0.0f ? exp2_fast(base - lse2) : 0.0f);
+    rsum = lt * to_ref + exp2_fast(sg - mr);
+  }
+  if (!q_valid) return;
+  if (dh == 0 && hh == 0) {
+    const int64_t ri = ((int64_t)b * a.n_heads_q + h) * a.seqlen_q + qi;
+    a.lse[ri] = lse2 * kLn2;
+    if (a.row_sum) a.row_sum[ri] = rsum;
+  }
+  // O row qi, dims dh*256 + db*32 + g*8 + hh*4 + {0..3}: 16-byte stores.
+  float* orow = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)qi * a.o_ss + dh * DH;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(f32x4*)(orow + db * 32 + g * 8 + hh * 4) =
+          f32x4{oacc[db][4 * g] * f, oacc[db][4 * g + 1] * f, oacc[db][4 * g + 2] * f,
+                oacc[db][4 * g + 3] * f};
+}
+
 template <int D, bool BF16>
 hipError_t launch_pack_d(const PrefillArgs& a, const VtArgs& w, hipStream_t stream) {
   constexpr int BN = tile_keys(D);
@@ -706,6 +945,20 @@ hipError_t launch_attn_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hip
   return hipGetLastError();
 }
 
+template <bool BF16>
+hipError_t launch_attn_512(const PrefillArgs& a, const VtArgs& w, bool unnorm, hipStream_t stream) {
+  const int per_group = a.n_heads_q / a.n_heads_kv;
+  const int nqb = (a.seqlen_q + 127) / 128;
+  const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group, nqb));
+  if (unnorm)
+    hipLaunchKernelGGL((prefill512_kernel<BF16, true>), grid, dim3(512), 0, stream, a,
+                       (const unsigned short*)w.ws);
+  else
+    hipLaunchKernelGGL((prefill512_kernel<BF16, false>), grid, dim3(512), 0, stream, a,
+                       (const unsigned short*)w.ws);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int head_dim) {
@@ -720,6 +973,7 @@ hipError_t launch_prefill_pack(const PrefillArgs& a, const VtArgs& w, int head_d
     case 64: return bf16 ? launch_pack_d<64, true>(a, w, stream) : launch_pack_d<64, false>(a, w, stream);
     case 128: return bf16 ? launch_pack_d<128, true>(a, w, stream) : launch_pack_d<128, false>(a, w, stream);
     case 256: return bf16 ? launch_pack_d<256, true>(a, w, stream) : launch_pack_d<256, false>(a, w, stream);
+    case 512: return bf16 ? launch_pack_d<512, true>(a, w, stream) : launch_pack_d<512, false>(a, w, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -736,6 +990,9 @@ hipError_t launch_prefill_attn(const PrefillArgs& a, const VtArgs& w, int head_d
     case 256:
       return bf16 ? launch_attn_d<256, true>(a, w, unnormalized, stream)
                   : launch_attn_d<256, false>(a, w, unnormalized, stream);
+    case 512:
+      return bf16 ? launch_attn_512<true>(a, w, unnormalized, stream)
+                  : launch_attn_512<false>(a, w, unnormalized, stream);
     default:
       return hipErrorInvalidValue;
   }

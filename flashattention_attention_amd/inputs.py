@@ -150,8 +150,13 @@ LARGE_HEAD = PrefillConfig("large_head_causal_prefill_b2_h16_d256_s8192_bf16_unn
 WINDOW_PREFILL = PrefillConfig("gqa_window1024_causal_prefill_b1_h28kv4_d128_s3314_bf16", 1, 28,
                                4, 128, 3314, 3314, "bf16", True, seed=6, window=1024)
 
+# A 512-wide head with every query head on one KV head (the head-dim budget
+# case of the FMHA notes' D1.4; their model is multi-query).
+HD512_PREFILL = PrefillConfig("mqa_hd512_causal_prefill_b1_h16kv1_d512_s4096_bf16", 1, 16, 1,
+                              512, 4096, 4096, "bf16", True, seed=7)
+
 WORKLOADS = {c.name: c for c in (TINY_CAUSAL, GQA_PREFILL, GQA_DECODE, LONG_DECODE, LARGE_HEAD,
-                                 WINDOW_PREFILL)}
+                                 WINDOW_PREFILL, HD512_PREFILL)}
 
 
 def make_prefill_inputs(cfg: PrefillConfig, seed: Optional[int] = None) -> dict:

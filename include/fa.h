@@ -81,7 +81,10 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  * device. window == 0 disables the window; window < 0 is rejected. The masks
  * combine freely (causal == 0 with a window admits every key after
  * p_i - window). A row that sees no key gets o = 0, row_sum = 0 and
- * lse = -inf.
+ * lse = -inf. Hidden keys that share a key tile (64 keys; 32 at head_dim
+ * 512) with visible ones are read and given weight zero, so K and V must hold
+ * finite values there too (V within fp16 range; padding past kv_lens[b]
+ * included); tiles with no visible key are skipped.
  *
  * sink_logits: DEVICE array [n_heads_q] of fp32 (4-byte aligned) or NULL. The
  * sink of query head h joins every row's softmax as one more term
@@ -89,10 +92,7 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  * the epilogue), so lse = ln(sum_j exp(s_ij) + exp(sink)), o is normalized by
  * that sum, and in un-normalized mode o and row_sum refer to
  * m_i = max(max_j s_ij, sink). A row with no key then gets o = 0,
- * lse = sink (row_sum = 1 in un-normalized mode). Hidden keys that share a 64-key tile with visible ones are read
- * and given weight zero, so K and V must hold finite values there too (V
- * within fp16 range; padding past kv_lens[b] included); tiles with no visible
- * key are skipped.
+ * lse = sink (row_sum = 1 in un-normalized mode).
  *
  * out_unnormalized == 0: o = normalized output; row_sum (optional) = l_i.
  * out_unnormalized != 0: o = sum_j P_ij v[j,:] with P_ij = exp(s_ij - m_i)
@@ -102,11 +102,12 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  * workspace: caller-owned device scratch of at least
  * fa_prefill_workspace_size(batch, seqlen_kv, n_heads_kv, head_dim) bytes,
  * 256-byte aligned. The call first repacks V into it (fp16, transposed per
- * 64-key tile), then runs the attention kernel; its contents are undefined
+ * key tile), then runs the attention kernel; its contents are undefined
  * afterwards and it must not be shared by calls that overlap in time.
  *
- * Supported set: head_dim in {64, 128, 256}; dtype FA_F16 or FA_BF16;
- * n_heads_q % n_heads_kv == 0; 1 <= seqlen_q <= seqlen_kv; batch >= 1;
+ * Supported set: head_dim in {64, 128, 256, 512} (512: "STAGE_D.md", D1.4,
+ * with the Q.K^T contraction split over a pair of waves); dtype FA_F16 or
+ * FA_BF16; n_heads_q % n_heads_kv == 0; 1 <= seqlen_q <= seqlen_kv; batch >= 1;
  * softmax_scale finite and > 0; q/k/v/o base pointers 16-byte aligned; q/k/v
  * stride_s, stride_h and stride_b multiples of 8, o strides multiples of 4;
  * k stride_s at most 2^23 elements.
@@ -188,8 +189,9 @@ int fa_attn_merge(const float* o_a, int64_t oa_sb, int64_t oa_ss, int64_t oa_sh,
 
 /*
  * fa_prefill_workspace_size — bytes of workspace fa_prefill_fwd needs
- * (batch * n_heads_kv * ceil(seqlen_kv / 64) * head_dim * 64 * 2). Returns 0
- * for non-positive sizes. Host only; never fails otherwise.
+ * (batch * n_heads_kv * ceil(seqlen_kv / T) * head_dim * T * 2, with tiles of
+ * T = 64 keys, 32 at head_dim 512). Returns 0 for non-positive sizes. Host
+ * only; never fails otherwise.
  */
 uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int head_dim);
 

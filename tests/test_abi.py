@@ -101,7 +101,7 @@ def _prefill(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(lse=None), 1), (dict(unnorm=1), 1),
     (dict(B=0), 1), (dict(Sq=0), 1), (dict(Skv=64), 1), (dict(Hkv=3), 1), (dict(Hq=0), 1),
-    (dict(D=96), 2), (dict(D=512), 2), (dict(dtype=7), 2),
+    (dict(D=96), 2), (dict(D=1024), 2), (dict(dtype=7), 2),
     (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=0.0), 1),
     (dict(scale=-1.0), 1), (dict(q=ALIGNED + 2), 1), (dict(o=ALIGNED + 4), 1),
     (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1), (dict(os=(128, 2, 128)), 1),
@@ -134,7 +134,7 @@ def test_prefill_pack_v_validation(kw, status):
 @pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(lse=None), 1), (dict(unnorm=1), 1),
-    (dict(Skv=64), 1), (dict(Hkv=3), 1), (dict(D=512), 2), (dict(scale=0.0), 1),
+    (dict(Skv=64), 1), (dict(Hkv=3), 1), (dict(D=1024), 2), (dict(scale=0.0), 1),
     (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1),
     (dict(win=-3), 1), (dict(lens=ALIGNED + 1), 1),
 ])
@@ -248,6 +248,7 @@ def test_workspace_size():
     assert lib.fa_prefill_workspace_size(2, 64, 1, 64) == 2 * 1 * 1 * 64 * 64 * 2
     assert lib.fa_prefill_workspace_size(1, 100, 2, 256) == 1 * 2 * 2 * 64 * 256 * 2
     assert lib.fa_prefill_workspace_size(0, 64, 1, 64) == 0
+    assert lib.fa_prefill_workspace_size(1, 100, 2, 512) == 1 * 2 * 4 * 32 * 512 * 2   # 32-key tiles
 
 
 def test_binding_rejects_cpu_tensors():
