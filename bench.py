@@ -12,8 +12,9 @@ both of its launches (V repack + attention), timed with HIP events (without
 system fence) on the launch stream; the roofline entry uses the attention
 launch alone. The same line carries the
 decode timings, the batched long-context decode (32 sequences, 512..32768
-tokens), the large-head prefill (head_dim 256, 8192 tokens) and the GQA prompt
-under a 1024-position sliding window as extra measurements, a roofline entry per kernel family, and the fp64 CPU oracle's
+tokens), the large-head prefill (head_dim 256, 8192 tokens), the GQA prompt
+under a 1024-position sliding window (with and without sinks) and a head_dim
+512 multi-query prefill as extra measurements, a roofline entry per kernel family, and the fp64 CPU oracle's
 throughput on a bounded sample of the prefill workload.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
@@ -125,6 +126,9 @@ def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None):
 
 def prefill_kernel_name(cfg):
     """The attention kernel's template name as rocprofv3 reports it."""
+    if cfg.head_dim == 512:
+        return (f"prefill512_kernel<{str(cfg.dtype == 'bf16').lower()}, "
+                f"{str(cfg.out_unnormalized).lower()}>")
     group = cfg.n_heads_q // cfg.n_heads_kv
     hp = 2 if cfg.head_dim <= 128 and group % 2 == 0 else 1
     return (f"prefill_kernel<{cfg.head_dim}, {str(cfg.dtype == 'bf16').lower()}, "
@@ -259,9 +263,9 @@ def run_profiling_aid(torch, fa, inputs, args):
         dst = torch.empty_like(src)
         fns = [lambda: dst.copy_(src)]
         label = f"copy {args.copy_bytes} bytes"
-    elif args.only in ("prefill", "large_head", "window"):
+    elif args.only in ("prefill", "large_head", "window", "hd512"):
         cfg = {"prefill": inputs.GQA_PREFILL, "large_head": inputs.LARGE_HEAD,
-               "window": inputs.WINDOW_PREFILL}[args.only]
+               "window": inputs.WINDOW_PREFILL, "hd512": inputs.HD512_PREFILL}[args.only]
         _, pack, attn = prefill_setup(torch, fa, cfg)
         fns, label = [pack, attn], cfg.name
     else:
@@ -287,7 +291,7 @@ def main():
     ap.add_argument("--split-sweep", action="store_true",
                     help="also time the single-token decode at several split lengths")
     ap.add_argument("--only", choices=["prefill", "decode", "long_decode", "large_head",
-                                              "window"],
+                                              "window", "hd512"],
                     help="profiling aid: run only this component (warmup + steps) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="profiling aid: time a plain device-to-device copy of this many "
@@ -537,6 +541,28 @@ def main():
             "us_per_launch": round(ru[2]["mean_ms"] * 1e3, 1),
             "per_launch": f"{merge_bytes / 1e6:.2f} MB (O and LSE read and written once)"}
         del s_pack, s_attn, p_pack2, p_attn2, s_merge, tens
+        print("[bench] head_dim 512 prefill", file=sys.stderr, flush=True)
+
+        xcfg = inputs.HD512_PREFILL
+        x_run, x_pack, x_attn = prefill_setup(torch, fa, xcfg)
+        x_run()
+        r = time_calls(torch, [x_pack, x_attn], 10)
+        xf = xcfg.flops()
+        x_ms = r[0]["mean_ms"] + r[1]["mean_ms"]
+        xa = xf / (r[1]["mean_ms"] * 1e-3) / 1e12
+        line["prefill_hd512"] = {"workload": xcfg.name, "us_per_call": round(x_ms * 1e3, 1),
+                                 "attention_us": round(r[1]["mean_ms"] * 1e3, 1),
+                                 "tflops": round(xf / (x_ms * 1e-3) / 1e12, 2),
+                                 "frac_mfma_peak": round(xf / (x_ms * 1e-3) / 1e12
+                                                         / MI355X_BF16_DENSE_TFLOPS, 4)}
+        xk = prefill_kernel_name(xcfg)
+        rooflines["prefill_hd512"] = {
+            "bound": "mfma", "achieved": round(xa, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(xa / MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": measured_traffic(xk, xcfg.name, "fa_prefill.hip"), "kernel": xk,
+            "us_per_launch": round(r[1]["mean_ms"] * 1e3, 1),
+            "per_launch": f"{xf / 1e12:.4f} TFLOP"}
+        del x_run, x_pack, x_attn
         del flush_buf
 
     line["roofline"] = rooflines["prefill_gqa_s3314"]
