@@ -268,10 +268,18 @@ def run_profiling_aid(torch, fa, inputs, args):
                "window": inputs.WINDOW_PREFILL, "hd512": inputs.HD512_PREFILL}[args.only]
         _, pack, attn = prefill_setup(torch, fa, cfg)
         fns, label = [pack, attn], cfg.name
+    elif args.only == "sink":
+        cfg = inputs.WINDOW_PREFILL
+        tens = {}
+        _, pack, attn = prefill_setup(torch, fa, cfg, tensors=tens)
+        sinks = torch.linspace(-2.0, 6.0, cfg.n_heads_q, dtype=torch.float32, device="cuda")
+        merge = fa.attn_merge(tens["o"], tens["lse"], sink_logits=sinks, out=tens["o"],
+                              lse=tens["lse"], prepare=True)
+        fns, label = [pack, attn, merge], cfg.name + "_sink"
     else:
         cfg = inputs.GQA_DECODE if args.only == "decode" else inputs.LONG_DECODE
-        part, merge, _ = decode_setup(torch, fa, cfg)
-        fns, label = [part, merge], cfg.name
+        part, merge, info = decode_setup(torch, fa, cfg)
+        fns, label = [part, merge, info["fused"]], cfg.name
     for _ in range(args.warmup):
         for f in fns:
             f()
@@ -291,7 +299,7 @@ def main():
     ap.add_argument("--split-sweep", action="store_true",
                     help="also time the single-token decode at several split lengths")
     ap.add_argument("--only", choices=["prefill", "decode", "long_decode", "large_head",
-                                              "window", "hd512"],
+                                              "window", "hd512", "sink"],
                     help="profiling aid: run only this component (warmup + steps) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="profiling aid: time a plain device-to-device copy of this many "
@@ -461,6 +469,17 @@ def main():
             "us_per_launch": round(r[0]["median_ms"] * 1e3, 1),
             "per_launch": f"{linfo['kv_bytes'] / 1e9:.4f} GB of K+V (each cached key and value "
                           f"row read once)"}
+        nw = fa.load_library().fa_decode_fused_waves(lcfg.head_dim, linfo["max_splits"])
+        fk = decode_kernel_name(lcfg).replace("decode_partial_kernel", "decode_fused_kernel")
+        fk = fk[:-1] + f", {nw}>"
+        f_gbps = linfo["kv_bytes"] / (fused_ms * 1e-3) / 1e9
+        rooflines["decode_fused_batched_long"] = {
+            "bound": "hbm", "achieved": round(f_gbps, 1), "peak": MI355X_HBM_GBPS,
+            "unit": "GB/s", "frac": round(f_gbps / MI355X_HBM_GBPS, 4),
+            "traffic": measured_traffic(fk, lcfg.name, "fa_decode.hip"), "kernel": fk,
+            "us_per_launch": round(fused_ms * 1e3, 1),
+            "per_launch": f"{linfo['kv_bytes'] / 1e9:.4f} GB of K+V (each cached key and value "
+                          f"row read once)"}
         del l_partial, l_merge, linfo
         torch.cuda.empty_cache()
         print("[bench] large-head prefill", file=sys.stderr, flush=True)
@@ -536,7 +555,9 @@ def main():
             "fused_tflops": round(wf / (fused_ms * 1e-3) / 1e12, 2)}
         rooflines["attn_merge_sink"] = {
             "bound": "hbm", "achieved": round(merge_gbps, 1), "peak": MI355X_HBM_GBPS,
-            "unit": "GB/s", "frac": round(merge_gbps / MI355X_HBM_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(merge_gbps / MI355X_HBM_GBPS, 4),
+            "traffic": measured_traffic("branch_merge_kernel<128>", wcfg.name + "_sink",
+                                        "fa_merge.hip"),
             "kernel": "branch_merge_kernel<128>",
             "us_per_launch": round(ru[2]["mean_ms"] * 1e3, 1),
             "per_launch": f"{merge_bytes / 1e6:.2f} MB (O and LSE read and written once)"}
