@@ -136,6 +136,8 @@ def prefill_kernel_name(cfg):
 
 
 def decode_kernel_name(cfg):
+    """The partial kernel's name for a decode that spans several rounds of
+    resident waves (the batched workload): the widest heads-per-wave choice."""
     group = cfg.n_heads_q // cfg.n_heads_kv
     g = next(x for x in range(8, 0, -1) if group % x == 0)
     return f"decode_partial_kernel<{cfg.head_dim}, {g}, {str(cfg.dtype == 'bf16').lower()}>"

@@ -289,7 +289,7 @@ int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_
       return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: kv_lens[%d] = %d < 1", b, kv_lens_host[b]);
     if (kv_lens_host[b] > max_len) max_len = kv_lens_host[b];
   }
-  const int g = fa::decode_heads_per_wave(n_heads_q / n_heads_kv);
+  const int g = fa::decode_max_heads_per_wave(n_heads_q / n_heads_kv);
   const int bk = fa::decode_block_rows(head_dim, g);
   const int64_t slots = (int64_t)num_cus * fa::decode_waves_per_cu(head_dim);
   const int64_t groups = n_heads_q / g;    // waves per (sequence, split)

@@ -4,10 +4,12 @@
 // bound by HBM bandwidth, not by the matrix cores. The partial kernel is
 // therefore plain VALU work arranged for bandwidth:
 //
-//  * one wave per (sequence, group of query heads sharing a KV head, split);
-//    the wave serves all query heads of the group, so each K/V row is read
-//    once for the whole group (the head packing of "STAGE_D.md — FMHA Kernel
-//    Development", section D2);
+//  * one wave per (sequence, set of query heads sharing a KV head, split);
+//    when the call needs more than one round of resident waves the wave
+//    serves up to 8 query heads of the group, so each K/V row is read once
+//    for all of them (the head packing of "STAGE_D.md — FMHA Kernel
+//    Development", section D2); when it fits in one round, fewer heads per
+//    wave shorten each wave's serial chain (decode_heads_per_wave);
 //  * a K or V row is spread over 16 lanes (8 lanes at head_dim 64) with 16
 //    contiguous bytes per lane, so one load instruction moves 4 whole rows
 //    (1 KB) per wave, fully coalesced;
@@ -598,7 +600,8 @@ int decode_fused_waves(int head_dim, int max_splits) {
 FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int head_dim,
                                 int max_splits) {
   FusedLayout f{};
-  const int g = decode_heads_per_wave(n_heads_q / n_heads_kv);
+  const int g = decode_heads_per_wave(n_heads_q / n_heads_kv, batch, n_heads_q, head_dim,
+                                      max_splits);
   f.waves = decode_fused_waves(head_dim, max_splits);
   f.max_wg = (max_splits + f.waves - 1) / f.waves;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -614,7 +617,8 @@ FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int he
 }
 
 hipError_t launch_decode_fused(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream) {
-  const int g = decode_heads_per_wave(a.n_heads_q / a.n_heads_kv);
+  const int g = decode_heads_per_wave(a.n_heads_q / a.n_heads_kv, a.batch, a.n_heads_q, head_dim,
+                                      a.max_splits);
   const int nw = decode_fused_waves(head_dim, a.max_splits);
   if ((a.max_splits + nw - 1) / nw != a.max_wg) return hipErrorInvalidValue;
   switch (head_dim) {
@@ -628,11 +632,24 @@ hipError_t launch_decode_fused(const DecodeArgs& a, int head_dim, bool bf16, hip
   }
 }
 
-// Heads served per wave: the largest divisor of the GQA group that is <= 8.
-int decode_heads_per_wave(int group) {
+// Heads served per wave. Serving several query heads of a KV head from one
+// wave reads each K/V row once for all of them, which is what a bandwidth-bound
+// decode needs; but when every wave fits in one round of resident waves the
+// call is latency-bound, and a wave's serial chain grows with its heads, so the
+// fewest heads per wave that keep the whole call within one round win (at 28/4
+// heads and 1641 keys: 10.0 us hot with one head per wave against 14.2 with
+// seven). A pure function of the shape, so the float results repeat.
+int decode_max_heads_per_wave(int group) {
   for (int g = 8; g >= 1; --g)
     if (group % g == 0) return g;
   return 1;
+}
+int decode_heads_per_wave(int group, int batch, int n_heads_q, int head_dim, int max_splits) {
+  const int gmax = decode_max_heads_per_wave(group);
+  const int64_t slots = (int64_t)kDecodeCus * decode_waves_per_cu(head_dim);
+  for (int g = 1; g < gmax; ++g)
+    if (group % g == 0 && (int64_t)batch * (n_heads_q / g) * max_splits <= slots) return g;
+  return gmax;
 }
 
 // Rows per block of the partial kernel and resident waves per compute unit
@@ -646,7 +663,8 @@ int decode_waves_per_cu(int head_dim) { return head_dim == 256 ? 4 : 8; }
 
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                                  hipStream_t stream) {
-  const int g = decode_heads_per_wave(a.n_heads_q / a.n_heads_kv);
+  const int g = decode_heads_per_wave(a.n_heads_q / a.n_heads_kv, a.batch, a.n_heads_q, head_dim,
+                                      a.max_splits);
   switch (head_dim) {
     case 64: return bf16 ? launch_partial_d<64, true>(a, g, stream)
                          : launch_partial_d<64, false>(a, g, stream);

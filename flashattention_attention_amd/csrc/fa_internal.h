@@ -104,8 +104,12 @@ struct FusedLayout {
 FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int head_dim,
                                 int max_splits);
 
-// Geometry of the decode partial kernel, for the split planner.
-int decode_heads_per_wave(int group);
+// Geometry of the decode partial kernel, for the split planner. Heads per wave
+// depend on the shape (see the definition); the planner steps split lengths in
+// blocks of the widest choice.
+constexpr int kDecodeCus = 256;   // compute units of the target GPU
+int decode_max_heads_per_wave(int group);
+int decode_heads_per_wave(int group, int batch, int n_heads_q, int head_dim, int max_splits);
 int decode_block_rows(int head_dim, int heads_per_wave);
 int decode_waves_per_cu(int head_dim);
 
