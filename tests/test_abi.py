@@ -256,3 +256,24 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros((1, 8, 1, 64), dtype=torch.float16)
     with pytest.raises(fa.FAError):
         fa.prefill(q, q, q)
+
+
+def test_binding_rejects_bad_host_arguments():
+    """The binding's own checks fire before any library call (no GPU needed)."""
+    import torch
+    o = torch.zeros((1, 4, 2, 64))
+    lse = torch.zeros((1, 2, 4))
+    with pytest.raises(fa.FAError):
+        fa.attn_merge(o, lse)                              # CPU tensors
+    with pytest.raises(fa.FAError):
+        fa.attn_merge(o, lse, o_b=o)                       # o_b without lse_b
+    q = torch.zeros((1, 4, 64), dtype=torch.float16)
+    kc = torch.zeros((8, 2, 64), dtype=torch.float16)
+    lens = torch.tensor([8], dtype=torch.int32)
+    offs = torch.tensor([0], dtype=torch.int64)
+    with pytest.raises(fa.FAError):
+        fa.decode_fused(q, kc, kc, offs, lens, split_len=16, max_splits=1)
+    with pytest.raises(fa.FAError):
+        fa.prefill(torch.zeros((1, 8, 2, 64), dtype=torch.float16),
+                   torch.zeros((1, 8, 1, 64), dtype=torch.float16),
+                   torch.zeros((1, 8, 1, 64), dtype=torch.float16), window=-1)
