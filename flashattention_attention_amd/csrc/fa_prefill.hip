@@ -400,9 +400,12 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
 
   // Loop-invariant LDS byte offsets of this lane's MFMA operands inside a stage.
   // (The K swizzle repeats every 16 rows, so block kb adds a constant kb*32 rows.)
-  int ka_off[NKK];
+  // The XOR swizzle touches only the low 4 bits of the chunk index, so k-step
+  // kk >= 8 is k-step kk - 8 plus 16 chunks: 8 offsets serve any head dim.
+  constexpr int NKO = NKK < 8 ? NKK : 8;
+  int ka_off[NKO];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
+  for (int kk = 0; kk < NKO; ++kk) {
     const int r = kh * KW + n;
     ka_off[kk] = r * KROW + (((2 * kk + hh) ^ (r & SWZ)) << 4);
   }
@@ -428,7 +431,8 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = mfma_qk<BF16>(*(const u32x4*)(kst + ka_off[kk] + kb * 32 * KROW), qr[kk], s[kb]);
+        s[kb] = mfma_qk<BF16>(
+            *(const u32x4*)(kst + ka_off[kk % 8] + (kk / 8) * 256 + kb * 32 * KROW), qr[kk], s[kb]);
   };
   // Mask, row max and (rarely) the move of the exponent base; returns the base.
   // Element i of block kb holds key t0 + kb*32 + (i/4)*8 + hh*4 + i%4.
@@ -561,10 +565,31 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
       if (t + 1 < ntiles) { issue_k(t + 1, ST_[1 - ST]); issue_v(t + 1, ST_[1 - ST] + KT); }
       f32x16 sc[NKB];
       qk(lds + ST_[ST], sc);
+      {
+        // Each MFMA's LDS operand read issued two MFMAs ahead of it (the
+        // compiler otherwise waits on every read right before its MFMA; more
+        // than two ahead costs registers this path does not have).
+        constexpr int NQ = NKB * NKK, AHEAD = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 2);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+          if (i + AHEAD < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        }
+      }
       const float base = prep(sc, (tb + t) * BN + kh * KW);
       u32x4 pk[NKS];
       expo(sc, base, pk);
       pv(lds + ST_[ST] + KT, pk);
+      {
+        constexpr int NP = NKS * NDB, AHEAD = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 3);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+          if (i + AHEAD < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+        }
+      }
       dma_wait();        // this wave's part of tile t+1 has landed
       __syncthreads();   // tile t+1 landed everywhere; stage ST is free for reuse
     };
