@@ -808,12 +808,21 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
+  // Each MFMA's LDS operand read is issued one MFMA ahead of it (left alone,
+  // the compiler waits on every read right before its MFMA; two ahead needs
+  // registers this kernel does not have).
   auto qk = [&](const char* kst, f32x16& s) {
     s = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       s = mfma_qk<BF16>(*(const u32x4*)(kst + ka8[kk % 8] + (dh * 32 + (kk / 8) * 16) * 16),
                         qr[kk], s);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NKK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + 1 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
   // Mask, row max and (rarely) the move of the exponent base, as in prefill_kernel.
   auto prep = [&](f32x16& s, int t0) -> float {
@@ -865,6 +874,13 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
       for (int db = 0; db < NDB; ++db)
         oacc[db] = mfma_pv(*(const u32x4*)(vst + va_off[ks] + db * 32 * (BN * 2)), pk[ks],
                            oacc[db]);
+    constexpr int NP = NKS * NDB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (i + 1 < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
   };
 
   // Plain double buffer: tile t+1 arrives while tile t is computed. Two
