@@ -147,6 +147,16 @@ __device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_addr) {
                : "memory");
 }
 
+// The same DMA from a wave-uniform base (held in scalar registers) plus a
+// 32-bit per-lane byte offset: one vector register per lane instead of a
+// 64-bit address, for kernels whose addresses would not stay in registers.
+__device__ __forceinline__ void dma16_at(const void* base, unsigned lane_bytes, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_bytes), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // V^T tile layout: D rows (head dims) x BN keys of fp16, BN*2 bytes per row
@@ -728,7 +738,7 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   constexpr int K_INSTR = BN / 8;            // K rows per wave per tile
   constexpr int V_INSTR = VT / 1024 / 8;
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE + 8 * 16 * 64 * 4];
-  float* xch = (float*)(lds + 2 * STAGE);    // [wave][element][lane] partial S^T
+  float* xch = (float*)(lds + 2 * STAGE);    // [wave][element/4][lane][4] partial S^T
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -781,16 +791,22 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   // position p (the swizzle that spreads an operand load over the banks).
   auto issue = [&](int t, unsigned st) {
     const int t0 = (tb + t) * BN;
+    // Recomputed per tile (one XOR each) rather than held across the loop:
+    // the loop has no registers to spare for four offsets.
+    unsigned lane16 = (unsigned)lane << 4;
+    asm volatile("" : "+v"(lane16));
 #pragma unroll
     for (int j = 0; j < K_INSTR; ++j) {
       const int r = wave * K_INSTR + j;
       const int key = min(t0 + r, a.seqlen_kv - 1);   // rows past the end: masked below
-      dma16(kp + (int64_t)key * a.k_ss + ((lane ^ (r & 15)) << 3), lds_base + st + r * KROW);
+      dma16_at(kp + (int64_t)key * a.k_ss, lane16 ^ ((unsigned)(r & 15) << 4),
+               lds_base + st + r * KROW);
     }
 #pragma unroll
     for (int j = 0; j < V_INSTR; ++j) {
       const int J = wave * V_INSTR + j;
-      dma16(vtp + (int64_t)(tb + t) * VT + J * 1024 + lane * 16, lds_base + st + KT + J * 1024);
+      dma16_at(vtp + (int64_t)(tb + t) * VT + J * 1024, (unsigned)lane << 4,
+               lds_base + st + KT + J * 1024);
     }
   };
 
@@ -893,10 +909,16 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     f32x16 s;
     qk(lds + ST_[ST], s);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xch[(wave * 16 + i) * 64 + lane] = s[i];
+    for (int c = 0; c < 4; ++c)
+      *(f32x4*)(xch + (wave * 4 + c) * 256 + lane * 4) = f32x4{s[4 * c], s[4 * c + 1],
+                                                              s[4 * c + 2], s[4 * c + 3]};
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] += xch[((wave ^ 4) * 16 + i) * 64 + lane];
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 p = *(const f32x4*)(xch + ((wave ^ 4) * 4 + c) * 256 + lane * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * c + e] += p[e];
+    }
     const float base = prep(s, (tb + t) * BN);
     u32x4 pk[NKS];
     expo(s, base, pk);
