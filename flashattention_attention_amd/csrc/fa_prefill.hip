@@ -371,40 +371,50 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
       (const unsigned short*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
   const char* vtp = (const char*)vt_ws + ((int64_t)b * a.n_heads_kv + hk) * ntiles_all * VT;
 
-  // Per-lane element offsets of this wave's K DMA rows inside a tile (the
-  // host guarantees BN * k_ss fits in 32 bits).
-  int koff[K_INSTR];
-#pragma unroll
-  for (int j = 0; j < K_INSTR; ++j) {
-    const int r = (wave * K_INSTR + j) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ (r & SWZ);
-    koff[j] = r * (int)a.k_ss + c * 8;
-  }
   const unsigned lds_base = (unsigned)(uintptr_t)(lptr_t)lds;
 
   // DMA of this wave's share of the K rows / V^T bytes of tile tb + t to LDS
-  // offset dst.
+  // offset dst. DMA instruction j of a wave writes rows R0 .. R0 + RPI - 1 of
+  // the tile (R0 = (wave * K_INSTR + j) * RPI, wave-uniform); lane l takes row
+  // R0 + l / CPR, logical chunk (l % CPR) ^ (row & SWZ). R0 is a multiple of
+  // RPI, so row & SWZ = (R0 & SWZ) ^ ((l / CPR) & SWZ): the lane part of the
+  // offset is the same for every j and the row base goes in scalar
+  // registers. The lane parts are rebuilt per tile (a few VALU) rather than
+  // held across the loop, which has no registers to spare for them. The
+  // ragged last tile clamps each lane's row instead (rows past the end repeat
+  // the last row; the mask zeroes them).
   auto issue_k = [&](int t, unsigned dst) {
     const int t0 = (tb + t) * BN;
-    const bool full = t0 + BN <= a.seqlen_kv;
+    unsigned ln = (unsigned)lane;
+    asm volatile("" : "+v"(ln));
+    const unsigned lrow = ln / CPR;
+    const unsigned lc16 = ((ln % CPR) ^ (lrow & SWZ)) << 4;
+    if (t0 + BN <= a.seqlen_kv) {
+      const unsigned lrow_b = lrow * (unsigned)a.k_ss * 2u;   // < 2^31 (k_ss <= 2^23)
 #pragma unroll
-    for (int j = 0; j < K_INSTR; ++j) {
-      const unsigned short* src;
-      if (full) {
-        src = kp + (int64_t)t0 * a.k_ss + koff[j];
-      } else {   // rows past the end repeat the last row; the mask zeroes them
-        const int r = (wave * K_INSTR + j) * RPI + lane / CPR;
-        const int key = min(t0 + r, a.seqlen_kv - 1);
-        src = kp + (int64_t)key * a.k_ss + (koff[j] - r * (int)a.k_ss);
+      for (int j = 0; j < K_INSTR; ++j) {
+        const int r0 = (wave * K_INSTR + j) * RPI;
+        dma16_at(kp + (int64_t)(t0 + r0) * a.k_ss, (lc16 ^ ((unsigned)(r0 & SWZ) << 4)) + lrow_b,
+                 lds_base + dst + (wave * K_INSTR + j) * 1024);
       }
-      dma16(src, lds_base + dst + (wave * K_INSTR + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < K_INSTR; ++j) {
+        const int r0 = (wave * K_INSTR + j) * RPI;
+        const int key = min(t0 + r0 + (int)lrow, a.seqlen_kv - 1);
+        dma16((const char*)(kp + (int64_t)key * a.k_ss) + (lc16 ^ ((unsigned)(r0 & SWZ) << 4)),
+              lds_base + dst + (wave * K_INSTR + j) * 1024);
+      }
     }
   };
   auto issue_v = [&](int t, unsigned dst) {
+    const char* base = vtp + (int64_t)(tb + t) * VT;
+    unsigned ln = (unsigned)lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int j = 0; j < V_INSTR; ++j) {
       const int J = wave * V_INSTR + j;
-      dma16(vtp + (int64_t)(tb + t) * VT + J * 1024 + lane * 16, lds_base + dst + J * 1024);
+      dma16_at(base + J * 1024, ln << 4, lds_base + dst + J * 1024);
     }
   };
 
