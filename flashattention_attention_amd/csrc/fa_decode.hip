@@ -1,8 +1,9 @@
 // Split-KV decode for gfx950: per-split partial attention and the LSE merge.
 //
-// Decode reads every K and V row once and does ~4 FLOP per byte, so it is
-// bound by HBM bandwidth, not by the matrix cores. The partial kernel is
-// therefore plain VALU work arranged for bandwidth:
+// Decode reads every K and V row once and does ~4 FLOP per byte per query
+// head it serves, so with few heads per K/V row it is bound by HBM bandwidth,
+// not by the matrix cores. The partial kernel is therefore VALU work arranged
+// for bandwidth:
 //
 //  * one wave per (sequence, set of query heads sharing a KV head, split);
 //    when the call needs more than one round of resident waves the wave
@@ -20,7 +21,11 @@
 //  * dot products use v_dot2 over packed halves, lane partial sums are
 //    reduced with DPP row permutes, and the online-softmax update is done
 //    once per block and head (section 3.2 of the same page gives the per-row
-//    form: new max, correction factor, exponential, running sum and output).
+//    form: new max, correction factor, exponential, running sum and output);
+//  * from 5 query heads per wave (head_dim <= 128) the per-head dot products
+//    and exponentials outweigh the loads, and Q.K^T moves to the matrix
+//    cores (split_attend_mfma): each K row then serves up to 16 heads in one
+//    16x16x32 MFMA, and the exponentials are spread one per (key, head).
 //
 // Each split emits a normalized partial O_s and its natural-log LSE_s. The
 // merge then combines the partials by LSE in a fixed order, so the result is
@@ -34,6 +39,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kSlack = 8.0f;   // stale-max tolerance (log2 units)
 constexpr float kLn2 = 0.693147180559945309f;
@@ -219,6 +226,207 @@ __device__ __forceinline__ void split_attend(const DecodeArgs& a, int b, int h0,
   }
 }
 
+// The same split with Q.K^T on the matrix cores, for waves that serve several
+// query heads (D <= 128). Per 32-key block:
+//  * S^T (16 keys x 16 heads per MFMA, v_mfma_f32_16x16x32) = K . Q^T: lane l
+//    loads K row l % 16 of a 16-key half, dims kk*32 + (l/16)*8 .. +7 (16
+//    contiguous bytes), and holds Q of head l % 16 for the same dims (zero for
+//    heads past G); it receives S for keys 4*(l/16) .. +3 of head l % 16;
+//  * the block max and the exponentials run in that layout: one exponential
+//    per (key, head) pair, wherever G is;
+//  * P (fp32) goes through a per-wave LDS buffer to the row layout of
+//    split_attend, whose P.V (fp32 FMAs on the half V elements) and final row-
+//    slot sums are unchanged.
+// pw: this wave's LDS scratch, kPRows * kPStride floats.
+constexpr int kPRows = 32;      // keys per block
+constexpr int kPStride = 20;    // floats per key row: 16 heads + 4 pad (no bank conflicts)
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Used from 5 heads per wave: there the VALU form is bound by its per-head
+// dot products and exponentials (at 32 cached keys per block, 4 KV heads and
+// 28 or 32 query heads the matrix-core form is 1.3-1.4x faster); at 3 and 4
+// heads both forms reach the same HBM rate and the VALU one is the leaner.
+__host__ __device__ constexpr bool decode_uses_mfma(int d, int g) { return d <= 128 && g >= 5; }
+
+template <int D, int G, bool BF16>
+__device__ __forceinline__ void split_attend_mfma(const DecodeArgs& a, int b, int h0, int lo,
+                                                  int hi, int lane, float* pw, float (&m)[G],
+                                                  float (&l)[G],
+                                                  float (&o)[G][D / lanes_per_row(D)]) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static_assert(G >= 1 && G <= 16, "at most 16 heads per wave");
+  constexpr int LPK = lanes_per_row(D);    // lanes per V row (row layout)
+  constexpr int EPL = D / LPK;
+  constexpr int W = EPL / 8;
+  constexpr int KPS = 64 / LPK;            // V rows per load step
+  constexpr int BK = kPRows;               // keys per block
+  constexpr int NB = BK / KPS;             // V load steps per block
+  constexpr int NKK = D / 32;              // MFMA k-steps
+  constexpr int NPV = (G + 3) / 4;         // 16-byte reads of one key's P row
+
+  const int hk = h0 / (a.n_heads_q / a.n_heads_kv);
+  const int slot = lane / LPK;
+  const int c = lane % LPK;
+  const int n = lane & 15;                 // MFMA column: query head h0 + n
+  const int quad = lane >> 4;              // MFMA lane group
+
+  u32x4 qop[NKK];
+  {
+    const unsigned short* qp = (const unsigned short*)a.q + (int64_t)b * a.q_sb +
+                               (int64_t)(h0 + min(n, G - 1)) * a.q_sh + quad * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qop[kk] = n < G ? *(const u32x4*)(qp + kk * 32) : u32x4{0, 0, 0, 0};
+  }
+
+  const int64_t row0 = a.kv_offsets[b];
+  const unsigned short* kq =
+      (const unsigned short*)a.k + row0 * a.kv_st + (int64_t)hk * a.kv_sh + quad * 8;
+  const unsigned short* vbase =
+      (const unsigned short*)a.v + row0 * a.kv_st + (int64_t)hk * a.kv_sh + c * EPL;
+
+  // One block: K in the MFMA layout (two 16-key halves), V in the row layout.
+  // Rows past hi repeat row hi-1 (valid memory); their scores are masked.
+  auto load_block = [&](int start, u32x4 (&kd)[2][NKK], u32x4 (&vd)[NB][W]) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int64_t key = min(start + sb * 16 + n, hi - 1);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        kd[sb][kk] = __builtin_nontemporal_load((const u32x4*)(kq + key * a.kv_st + kk * 32));
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int64_t key = min(start + j * KPS + slot, hi - 1);
+#pragma unroll
+      for (int w = 0; w < W; ++w)
+        vd[j][w] = __builtin_nontemporal_load((const u32x4*)(vbase + key * a.kv_st + w * 8));
+    }
+  };
+
+  float mc = -1e30f;   // running max (log2 units) of head column n
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
+  }
+
+  auto compute_block = [&](int start, const u32x4 (&kd)[2][NKK], const u32x4 (&vd)[NB][W]) {
+    f32x4 s[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) s[sb] = mfma16<BF16>(kd[sb][kk], qop[kk], s[sb]);
+    }
+    if (start + BK > hi) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (start + sb * 16 + quad * 4 + i >= hi) s[sb][i] = -INFINITY;
+    }
+    // Block max of head column n: in-lane over 8 keys, then over the 4 lane groups.
+    float lm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    lm = fmaxf(lm, __shfl_xor(lm, 16));
+    lm = fmaxf(lm, __shfl_xor(lm, 32));
+    const float bm = lm * a.scale_log2;    // the max commutes with the positive scale
+    const bool grow = bm > mc + kSlack;
+    if (__ballot(grow)) {
+      const float nm = grow ? bm : mc;
+      const float corr = __builtin_amdgcn_exp2f(mc - nm);
+      mc = nm;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float cg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), g));
+        l[g] *= cg;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] *= cg;
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pw[(sb * 16 + quad * 4 + i) * kPStride + n] =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], a.scale_log2, -mc));
+    // Other lanes' P values are read below: the writes must have landed.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float* pr = pw + (j * KPS + slot) * kPStride;
+      float p[4 * NPV];
+#pragma unroll
+      for (int r = 0; r < NPV; ++r) {
+        const f32x4 v4 = *(const f32x4*)(pr + 4 * r);
+        p[4 * r] = v4[0];
+        p[4 * r + 1] = v4[1];
+        p[4 * r + 2] = v4[2];
+        p[4 * r + 3] = v4[3];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        l[g] += p[g];
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[g][w * 8 + 2 * e] = __builtin_fmaf(p[g], half_lo<BF16>(vd[j][w][e]),
+                                                 o[g][w * 8 + 2 * e]);
+            o[g][w * 8 + 2 * e + 1] = __builtin_fmaf(p[g], half_hi<BF16>(vd[j][w][e]),
+                                                     o[g][w * 8 + 2 * e + 1]);
+          }
+      }
+    }
+    // The next block's P writes must not overtake these reads.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  u32x4 ka[2][NKK], kb[2][NKK], va[NB][W], vb[NB][W];
+  load_block(lo, ka, va);
+  for (int start = lo; start < hi; start += 2 * BK) {
+    if (start + BK < hi) load_block(start + BK, kb, vb);
+    compute_block(start, ka, va);
+    if (start + BK >= hi) break;
+    if (start + 2 * BK < hi) load_block(start + 2 * BK, ka, va);
+    compute_block(start + BK, kb, vb);
+  }
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mc), g));
+#pragma unroll
+    for (int x = LPK; x < 64; x *= 2) {
+      l[g] += __shfl_xor(l[g], x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[g][e] += __shfl_xor(o[g][e], x);
+    }
+  }
+}
+
+// The split of one wave by whichever form serves its (D, G); pw is used by
+// the matrix-core form only.
+template <int D, int G, bool BF16>
+__device__ __forceinline__ void split_run(const DecodeArgs& a, int b, int h0, int lo, int hi,
+                                         int lane, float* pw, float (&m)[G], float (&l)[G],
+                                         float (&o)[G][D / lanes_per_row(D)]) {
+  if constexpr (decode_uses_mfma(D, G))
+    split_attend_mfma<D, G, BF16>(a, b, h0, lo, hi, lane, pw, m, l, o);
+  else
+    split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
+}
+
 // One wave per (sequence, group of G query heads, split): the split's
 // normalized partial output and its natural-log LSE.
 template <int D, int G, bool BF16>
@@ -236,8 +444,9 @@ decode_partial_kernel(DecodeArgs a) {
   const int hi = min(L, lo + a.split_len);
   const int slot = lane / LPK;
   const int c = lane % LPK;
+  __shared__ __attribute__((aligned(16))) float pbuf[decode_uses_mfma(D, G) ? kPRows * kPStride : 1];
   float m[G], l[G], o[G][EPL];
-  split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
+  split_run<D, G, BF16>(a, b, h0, lo, hi, lane, pbuf, m, l, o);
   if (slot == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -346,6 +555,7 @@ decode_fused_kernel(DecodeArgs a) {
   __shared__ float so[NW][G][D];
   __shared__ float sm[NW][G], sl[NW][G];
   __shared__ int is_last;
+  __shared__ __attribute__((aligned(16))) float pbuf[NW][decode_uses_mfma(D, G) ? kPRows * kPStride : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hg = blockIdx.x, h0 = hg * G, y = blockIdx.y, b = blockIdx.z;
@@ -360,7 +570,7 @@ decode_fused_kernel(DecodeArgs a) {
     const int lo = (y * NW + wave) * a.split_len;
     const int hi = min(L, lo + a.split_len);
     float m[G], l[G], o[G][EPL];
-    split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
+    split_run<D, G, BF16>(a, b, h0, lo, hi, lane, pbuf[wave], m, l, o);
     if (lane < LPK) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
