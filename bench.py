@@ -471,7 +471,8 @@ def main():
             "us_per_launch": round(r[0]["median_ms"] * 1e3, 1),
             "per_launch": f"{linfo['kv_bytes'] / 1e9:.4f} GB of K+V (each cached key and value "
                           f"row read once)"}
-        nw = fa.load_library().fa_decode_fused_waves(lcfg.head_dim, linfo["max_splits"])
+        nw = fa.load_library().fa_decode_fused_waves(lcfg.batch, lcfg.n_heads_q, lcfg.n_heads_kv,
+                                                     lcfg.head_dim, linfo["max_splits"])
         fk = decode_kernel_name(lcfg).replace("decode_partial_kernel", "decode_fused_kernel")
         fk = fk[:-1] + f", {nw}>"
         f_gbps = linfo["kv_bytes"] / (fused_ms * 1e-3) / 1e9

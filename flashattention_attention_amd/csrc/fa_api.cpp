@@ -447,9 +447,12 @@ uint64_t fa_decode_fused_workspace_size(int batch, int n_heads_q, int n_heads_kv
   return fa::decode_fused_layout(batch, n_heads_q, n_heads_kv, head_dim, max_splits).total;
 }
 
-int fa_decode_fused_waves(int head_dim, int max_splits) {
-  if (!head_dim_supported(head_dim) || max_splits < 1) return 0;
-  return fa::decode_fused_waves(head_dim, max_splits);
+int fa_decode_fused_waves(int batch, int n_heads_q, int n_heads_kv, int head_dim,
+                          int max_splits) {
+  if (batch < 1 || n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0 ||
+      !head_dim_supported(head_dim) || max_splits < 1)
+    return 0;
+  return fa::decode_fused_waves(batch, n_heads_q, n_heads_kv, head_dim, max_splits);
 }
 
 int fa_decode_merge_lse(const float* part_o, const float* part_lse, const int32_t* kv_lens,

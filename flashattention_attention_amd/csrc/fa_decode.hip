@@ -796,15 +796,21 @@ hipError_t launch_fused_d(const DecodeArgs& a, int g, int nw, hipStream_t stream
 
 }  // namespace
 
-// Few splits per sequence (long splits, bandwidth-bound): one wave per
-// work-group, so no compute unit slot waits on a sibling wave with no split;
-// many (short, latency-bound splits): merge groups of 4 on chip first, so the
-// last work-group merges few partials (measured at 28/4 heads and 1641
-// tokens: 4 waves beat 2 and 8, which packs the latency-bound waves onto too
-// few compute units).
-int decode_fused_waves(int head_dim, int max_splits) {
-  (void)head_dim;
-  return max_splits <= 16 ? 1 : 4;
+// Work-group size of the single-launch decode. A call that needs more than one
+// round of resident waves is bandwidth-bound: one wave per work-group, so no
+// compute unit slot waits on a sibling wave's split, and the one merge at the
+// end is cheap next to the streaming (4 KV heads, 28 or 32 query heads, 25
+// splits of 1296 tokens: 295 / 314 us with one wave against 355 / 371 with
+// four). A call that fits in one round and has many short splits is
+// latency-bound: groups of 4 merge on chip first, so the last work-group
+// merges few partials (28/4 heads, 1641 tokens: 4 waves beat 2 and 8, which
+// packs the latency-bound waves onto too few compute units).
+int decode_fused_waves(int batch, int n_heads_q, int n_heads_kv, int head_dim, int max_splits) {
+  if (max_splits <= 16) return 1;
+  const int g = decode_heads_per_wave(n_heads_q / n_heads_kv, batch, n_heads_q, head_dim,
+                                      max_splits);
+  const int64_t slots = (int64_t)kDecodeCus * decode_waves_per_cu(head_dim);
+  return (int64_t)batch * (n_heads_q / g) * max_splits <= slots ? 4 : 1;
 }
 
 FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int head_dim,
@@ -812,7 +818,7 @@ FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int he
   FusedLayout f{};
   const int g = decode_heads_per_wave(n_heads_q / n_heads_kv, batch, n_heads_q, head_dim,
                                       max_splits);
-  f.waves = decode_fused_waves(head_dim, max_splits);
+  f.waves = decode_fused_waves(batch, n_heads_q, n_heads_kv, head_dim, max_splits);
   f.max_wg = (max_splits + f.waves - 1) / f.waves;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   // The counters sit in a fixed region at the start, whatever the shape, so a
@@ -829,7 +835,7 @@ FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int he
 hipError_t launch_decode_fused(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   const int g = decode_heads_per_wave(a.n_heads_q / a.n_heads_kv, a.batch, a.n_heads_q, head_dim,
                                       a.max_splits);
-  const int nw = decode_fused_waves(head_dim, a.max_splits);
+  const int nw = decode_fused_waves(a.batch, a.n_heads_q, a.n_heads_kv, head_dim, a.max_splits);
   if ((a.max_splits + nw - 1) / nw != a.max_wg) return hipErrorInvalidValue;
   switch (head_dim) {
     case 64: return bf16 ? launch_fused_d<64, true>(a, g, nw, stream)

@@ -93,7 +93,7 @@ hipError_t launch_decode_fused(const DecodeArgs& a, int head_dim, bool bf16, hip
 hipError_t launch_branch_merge(const BranchMergeArgs& a, int head_dim, hipStream_t stream);
 
 // Splits (one per wave) merged inside one work-group of the single-launch decode.
-int decode_fused_waves(int head_dim, int max_splits);
+int decode_fused_waves(int batch, int n_heads_q, int n_heads_kv, int head_dim, int max_splits);
 // Workspace of the single-launch decode, and the offsets of its parts.
 constexpr size_t kFusedCounterBytes = 65536;   // room for 16384 arrival counters
 struct FusedLayout {

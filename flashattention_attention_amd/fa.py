@@ -49,7 +49,7 @@ _SIGNATURES = {
                          _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp,
                          _vp, ctypes.c_uint64, _vp], _i32),
     "fa_decode_fused_workspace_size": ([_i32, _i32, _i32, _i32, _i32], ctypes.c_uint64),
-    "fa_decode_fused_waves": ([_i32, _i32], _i32),
+    "fa_decode_fused_waves": ([_i32, _i32, _i32, _i32, _i32], _i32),
     "fa_status_string": ([_i32], ctypes.c_char_p),
     "fa_last_error": ([], ctypes.c_char_p),
 }

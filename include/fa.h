@@ -281,8 +281,9 @@ int fa_decode_merge_lse(const float* part_o, const float* part_lse, const int32_
  *
  * Computes what fa_decode_split_partial followed by fa_decode_merge_lse
  * computes (same arguments, same split partition, o and lse as written by the
- * merge), in one kernel: each work-group of W = fa_decode_fused_waves(head_dim,
- * max_splits) waves (1 when max_splits <= 16, else 4)
+ * merge), in one kernel: each work-group of W = fa_decode_fused_waves(batch,
+ * n_heads_q, n_heads_kv, head_dim, max_splits) waves (4 when the call has more
+ * than 16 splits and fits in one round of resident waves, else 1)
  * takes W consecutive splits of one sequence and merges them on chip; when
  * one work-group covers every split of a sequence its merge is the output,
  * otherwise the last work-group of the sequence to finish merges the
@@ -318,7 +319,8 @@ int fa_decode_fused(const void* q, int64_t q_sb, int64_t q_sh,
  */
 uint64_t fa_decode_fused_workspace_size(int batch, int n_heads_q, int n_heads_kv, int head_dim,
                                         int max_splits);
-int fa_decode_fused_waves(int head_dim, int max_splits);
+int fa_decode_fused_waves(int batch, int n_heads_q, int n_heads_kv, int head_dim,
+                          int max_splits);
 
 /* Static text for a status code. */
 const char* fa_status_string(int status);

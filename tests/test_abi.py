@@ -206,16 +206,24 @@ def test_decode_fused_validation(kw, status):
 
 def test_decode_fused_workspace_size():
     lib = fa.load_library()
-    assert lib.fa_decode_fused_waves(128, 52) == 4 and lib.fa_decode_fused_waves(256, 52) == 4
-    assert lib.fa_decode_fused_waves(128, 16) == 1 and lib.fa_decode_fused_waves(96, 4) == 0
+    # one round of resident waves and more than 16 splits: groups of 4 (latency-bound)
+    assert lib.fa_decode_fused_waves(1, 28, 4, 128, 52) == 4
+    assert lib.fa_decode_fused_waves(1, 28, 4, 256, 52) == 4
+    # 16 splits or fewer, or more than one round (bandwidth-bound): one wave
+    assert lib.fa_decode_fused_waves(1, 28, 4, 128, 16) == 1
+    assert lib.fa_decode_fused_waves(32, 28, 4, 128, 25) == 1      # 32 x 4 x 25 > 2048
+    assert lib.fa_decode_fused_waves(2, 28, 4, 128, 25) == 4       # 2 x 28 x 25 <= 2048
+    assert lib.fa_decode_fused_waves(1, 28, 4, 96, 4) == 0
+    assert lib.fa_decode_fused_waves(1, 28, 3, 128, 4) == 0
 
     def up(x):
         return (x + 255) // 256 * 256
     # 1 sequence, 28/4 heads (7 per wave -> 4 head groups), 52 splits -> 13 work-groups
     want = 65536 + up(28 * 13 * 4) + up(28 * 13 * 128 * 4)     # fixed counter region first
     assert lib.fa_decode_fused_workspace_size(1, 28, 4, 128, 52) == want
-    # 32 sequences, 32/8 heads (4 per wave), head_dim 256, 40 splits -> 4 per work-group
-    want = 65536 + up(32 * 32 * 10 * 4) + up(32 * 32 * 10 * 256 * 4)
+    # 32 sequences, 32/8 heads (4 per wave), head_dim 256, 40 splits: more than one
+    # round of resident waves -> one split per work-group
+    want = 65536 + up(32 * 32 * 40 * 4) + up(32 * 32 * 40 * 256 * 4)
     assert lib.fa_decode_fused_workspace_size(32, 32, 8, 256, 40) == want
     # 13 splits: one per work-group
     want = 65536 + up(32 * 32 * 13 * 4) + up(32 * 32 * 13 * 128 * 4)
