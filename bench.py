@@ -167,10 +167,14 @@ def measured_traffic(kernel, workload, source):
     return None
 
 
-def decode_setup(torch, fa, cfg, split_len=None):
+def decode_setup(torch, fa, cfg, split_len=None, head_major=False):
+    """head_major: the same caches stored [Hkv, T, D] (passed as [T, Hkv, D] views
+    with a head stride of T*D); the default is token-major [T, Hkv, D]."""
     from flashattention_attention_amd import inputs
     x = inputs.make_decode_inputs(cfg)
     q, kc, vc = (_dev(torch, x[n], cfg.dtype) for n in ("q", "k_cache", "v_cache"))
+    if head_major:
+        kc, vc = (t.permute(1, 0, 2).contiguous().permute(1, 0, 2) for t in (kc, vc))
     offs = torch.from_numpy(x["kv_offsets"]).cuda()
     lens = torch.from_numpy(x["kv_lens"]).cuda()
     if split_len is None:
@@ -463,6 +467,17 @@ def main():
             "fused_frac_hbm_peak": round(linfo["alg_bytes"] / (fused_ms * 1e-3) / 1e9
                                          / MI355X_HBM_GBPS, 4),
             "cache": "flushed (512 MB write) before every call"}
+        # The same decode on head-major caches (each wave's K and V rows then
+        # lie in one contiguous stream instead of every Hkv-th 256 bytes).
+        h_partial, h_merge, _ = decode_setup(torch, fa, lcfg, head_major=True)
+        for _ in range(3):
+            h_partial(); h_merge()
+        rh = time_calls(torch, [h_partial, h_merge], 20, flush=flush)
+        h_ms = rh[0]["median_ms"] + rh[1]["median_ms"]
+        line["decode_batched_long"]["head_major_caches"] = {
+            "us_per_call": round(h_ms * 1e3, 1), "partial_us": round(rh[0]["median_ms"] * 1e3, 1),
+            "frac_hbm_peak": round(linfo["alg_bytes"] / (h_ms * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4)}
+        del h_partial, h_merge
         dk = decode_kernel_name(lcfg)
         rooflines["decode_partial_batched_long"] = {
             "bound": "hbm", "achieved": round(part_gbps, 1), "peak": MI355X_HBM_GBPS,

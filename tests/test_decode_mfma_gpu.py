@@ -6,10 +6,12 @@ online update) and "STAGE_D.md — FMHA Kernel Development", section D2 (several
 query heads packed on one K/V stream). Same gate as every decode test: |O|
 error <= 2e-3, natural-log LSE error <= 1e-4, byte-identical repeats.
 
-The shapes are sized so that the heads-per-wave rule takes the whole GQA group
-(the call spans more than one round of resident waves at any smaller divisor):
-8 sequences x ceil(max_len / split_len) splits x (Hq / g) waves > 2048 for
-every divisor g below the group.
+The shapes of the matrix-core cases are sized so that the heads-per-wave rule
+takes the whole GQA group (the call spans more than one round of resident
+waves at any smaller divisor): 8 sequences x ceil(max_len / split_len) splits
+x (Hq / g) waves > 2048 for every divisor g below the group. The last test
+checks that head-major caches (any kv_stride_head / kv_stride_tok) give the
+same bytes as token-major ones, in both decode forms.
 """
 import numpy as np
 import pytest
@@ -104,3 +106,45 @@ def test_decode_matrix_core_form(torch_gpu, dtype, D, hq, hkv, split_len, k_mult
     hk_of = np.arange(hq) // (hq // hkv)
     v0 = inputs.half_bits_to_f32(vc[0], dtype)[hk_of]
     np.testing.assert_allclose(o[0], v0, atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv,split_len,want_g", [
+    ("f16", 128, 28, 4, 32, 7),     # matrix-core form
+    ("bf16", 128, 32, 8, 32, 4),    # VALU form, 4 heads per wave
+    ("f16", 64, 8, 8, 48, 1),       # VALU form, one head per wave
+])
+def test_decode_head_major_caches(torch_gpu, dtype, D, hq, hkv, split_len, want_g):
+    """Caches stored head-major ([Hkv, T, D], passed through kv_stride_head = T*D
+    and kv_stride_tok = D) give byte-identical results to the token-major ones:
+    the kernels read the same values in the same order."""
+    from flashattention_attention_amd import fa
+    torch = torch_gpu
+    rng = np.random.default_rng(D + hq * 3 + split_len)
+    lens = np.array([1, 17, 32, 333, 700, 1000, 1231, 1300], np.int32)
+    B = len(lens)
+    max_splits = -(-int(lens.max()) // split_len)
+    assert _heads_per_wave(hq // hkv, B, hq, max_splits) == want_g
+    _say("head-major caches", dtype, D, hq, hkv, split_len)
+    offs = np.concatenate([[0], np.cumsum(lens.astype(np.int64))[:-1]]).astype(np.int64)
+    T = int(lens.sum())
+    q = inputs.draw_half(rng, (B, hq, D), dtype)
+    kc = inputs.draw_half(rng, (T, hkv, D), dtype)
+    vc = inputs.draw_half(rng, (T, hkv, D), dtype)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    qd, kd, vd = _dev(torch, q, dtype), _dev(torch, kc, dtype), _dev(torch, vc, dtype)
+    khm, vhm = (t.permute(1, 0, 2).contiguous().permute(1, 0, 2) for t in (kd, vd))
+    assert khm.stride() == (D, T * D, 1)
+    od, ld = torch.from_numpy(offs).cuda(), torch.from_numpy(lens).cuda()
+    outs = []
+    for k, v in ((kd, vd), (khm, vhm)):
+        o, lse = fa.decode(qd, k, v, od, ld, split_len=split_len, max_splits=max_splits,
+                           softmax_scale=scale)
+        of, lsef = fa.decode_fused(qd, k, v, od, ld, split_len=split_len,
+                                   max_splits=max_splits, softmax_scale=scale)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (o, lse, of, lsef)])
+    for a, b in zip(*outs):
+        assert a.tobytes() == b.tobytes()
+    ref = oracle.decode(q, kc, vc, offs, lens, scale=scale, dtype=dtype)
+    assert np.abs(outs[1][0] - ref["o"]).max() <= O_TOL
+    assert np.abs(outs[1][1] - ref["lse"]).max() <= LSE_TOL
