@@ -4,7 +4,7 @@
 //
 //  1. vt_pack_kernel: V [B, Skv, Hkv, D] (fp16 or bf16) -> fp16 V^T tiles in
 //     the caller's workspace, laid out [B][Hkv][tile][D][T keys] (T = 64;
-//     32 at head_dim 512), keys in
+//     32 at head_dim 256 and 512), keys in
 //     the order the P.V
 //     contraction consumes them, 16-byte chunks XOR-swizzled inside every
 //     row, and zero-filled keys past Skv. bf16 V is converted to fp16 here, once, instead of in every
@@ -12,13 +12,13 @@
 //     range).
 //
 //  2. prefill_kernel: one work-group per (query block, query head, batch);
-//     2 waves per SIMD. At head_dim <= 128 a work-group has 4 waves, each
-//     owning 32 query rows (128 per block) and taking whole 64-key tiles, and
-//     two work-groups share a compute unit. At head_dim 256 a work-group has
-//     8 waves: waves w and w+4 own the same 32 rows (128 per block), each
-//     takes half of every tile with its own online softmax, and the pair is
-//     merged at the end. Head_dim 512 has its own kernel (prefill512_kernel)
-//     in which the two waves of a pair split the head dimension instead.
+//     2 waves per SIMD. A work-group has 4 waves, each owning 32 query rows
+//     (128 per block) and taking whole tiles of keys (64-key tiles up to
+//     head_dim 128, 32-key tiles at head_dim 256), and two work-groups share
+//     a compute unit (or, when two query heads of a KV head are paired at
+//     head_dim <= 128, one work-group of 8 waves; see wg_waves). Head_dim 512
+//     has its own kernel (prefill512_kernel) in which the two waves of a pair
+//     split the head dimension.
 //
 // Mapping to the CDNA4 matrix cores (v_mfma_f32_32x32x16_{bf16,f16}): each
 // wave computes the TRANSPOSED score tile S^T = K . Q^T (keys along M, its 32
@@ -77,22 +77,19 @@ constexpr float kSlack = 8.0f;            // stale-max tolerance (log2 units)
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
 
-// Work-group geometry per head dim. key_split(d) = 1: every wave owns its own
-// 32 query rows and takes whole 64-key tiles. key_split(d) = 2 (head_dim 256,
-// where a wave cannot hold 64 keys of scores next to its Q and O registers):
-// waves w and w+4 own the same 32 query rows and each takes half of every
-// tile.
-__host__ __device__ constexpr int key_split(int d) { return d <= 128 ? 1 : 2; }
+// Work-group geometry per head dim. Every wave owns 32 query rows of one
+// query head and takes whole tiles of keys: 64-key tiles up to head_dim 128,
+// 32-key tiles at head_dim 256 (a wave cannot hold 64 keys of scores next to
+// its Q and O registers there; 32-key tiles also keep the two tile stages at
+// 64 KB, so two work-groups share a compute unit) and at head_dim 512.
 // Query heads per work-group (hp): at head_dim <= 128, when the query heads
 // that share a KV head come in pairs, a work-group serves the same 128 query
 // rows of two of them, so every K and V^T tile brought into LDS feeds eight
 // waves while the causal extent of a work-group stays that of 128 rows.
-// Waves per work-group: 4 per query head at head_dim <= 128 (32 rows each),
-// 8 at head_dim 256 (four wave pairs).
-__host__ __device__ constexpr int wg_waves(int d, int hp) { return d <= 128 ? 4 * hp : 8; }
-__host__ __device__ constexpr int tile_keys(int d) {
-  return d == 512 ? 32 : (key_split(d) == 1 ? 64 : (d <= 128 ? 128 : 64));
-}
+// Waves per work-group: 4 per query head (32 rows each) up to head_dim 256;
+// head_dim 512 has its own kernel.
+__host__ __device__ constexpr int wg_waves(int d, int hp) { return d <= 256 ? 4 * hp : 8; }
+__host__ __device__ constexpr int tile_keys(int d) { return d <= 128 ? 64 : 32; }
 __host__ __device__ constexpr int block_rows(int d) { return 128; }
 
 template <bool BF16>
@@ -285,14 +282,12 @@ __global__ void __launch_bounds__(64 * wg_waves(D, HP)) __attribute__((amdgpu_wa
 prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   constexpr int kWaves = wg_waves(D, HP);
   constexpr bool PIPE = D <= 128;            // software-pipelined loop (register budget)
-  constexpr int KS = key_split(D);           // waves sharing one query group
   constexpr int QG = 4;                      // query groups of 32 rows per head
-  static_assert(kWaves == HP * KS * QG, "work-group shape");
+  static_assert(kWaves == HP * QG, "work-group shape");
   constexpr int kBM = 32 * QG;               // query rows per work-group
   constexpr int BN = tile_keys(D);           // keys per tile
-  constexpr int KW = BN / KS;                // keys per wave per tile
-  constexpr int NKB = KW / 32;               // 32-key MFMA blocks per wave per tile
-  constexpr int NKS = KW / 16;               // MFMA k-steps of P.V per tile
+  constexpr int NKB = BN / 32;               // 32-key MFMA blocks per tile
+  constexpr int NKS = BN / 16;               // MFMA k-steps of P.V per tile
   constexpr int NKK = D / 16;                // MFMA k-steps of Q.K^T
   constexpr int NDB = D / 32;                // 32-row blocks of O^T
   constexpr int KROW = D * 2;                // bytes per K row
@@ -305,23 +300,20 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   constexpr int K_INSTR = KT / 1024 / kWaves;   // DMA instructions per wave per tile
   constexpr int V_INSTR = VT / 1024 / kWaves;
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile too small for the DMA split");
-  static_assert(KS == 1 || 4 * NDB * 16 * 64 * 4 <= 2 * STAGE, "LDS too small for the pair merge");
-  static_assert(KS == 1 || NDB * 16 * 64 * 4 == 32 * D * 4, "merge slice must hold 32 O rows");
 
-  // K/V^T tiles (two of each); after the loop, the per-wave O staging area
-  // (32 rows x D fp32 per wave; at key_split 2 a pair leader reuses its own
-  // merge slice, which has exactly that size).
-  constexpr int OSTG = 32 * D * 4;
-  constexpr int LDS_BYTES = (KS == 1 && kWaves * OSTG > 2 * STAGE) ? kWaves * OSTG : 2 * STAGE;
+  // K/V^T tiles (two stages); after the loop, the per-wave O staging area
+  // (32 rows x D / OH fp32 per wave).
+  constexpr int OH = D > 128 ? 2 : 1;        // O rows staged in OH parts of D / OH dims
+  constexpr int DP = D / OH;
+  constexpr int OSTG = 32 * DP * 4;
+  constexpr int LDS_BYTES = kWaves * OSTG > 2 * STAGE ? kWaves * OSTG : 2 * STAGE;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
-  __shared__ float xs[KS == 2 ? 2 * 4 * 3 * 64 : 1];   // per-row softmax state, for the pair merge
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qw = wave % QG;               // which 32 query rows
-  const int kh = (wave / QG) % KS;        // which part of every tile
-  const int hp = wave / (QG * KS);        // which query head of the work-group
+  const int hp = wave / QG;               // which query head of the work-group
   const int nqb = (a.seqlen_q + kBM - 1) / kBM;
   const int per_group = a.n_heads_q / a.n_heads_kv;
   const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nqb);
@@ -426,13 +418,12 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   int ka_off[NKO];
 #pragma unroll
   for (int kk = 0; kk < NKO; ++kk) {
-    const int r = kh * KW + n;
-    ka_off[kk] = r * KROW + (((2 * kk + hh) ^ (r & SWZ)) << 4);
+    ka_off[kk] = n * KROW + (((2 * kk + hh) ^ (n & SWZ)) << 4);
   }
   int va_off[NKS];   // + db * 32 rows for head-dim block db (the swizzle repeats every 16 rows)
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
-    va_off[ks] = vt_chunk_offset<BN>(n, kh * (KW / 8) + ks * 2 + hh);
+    va_off[ks] = vt_chunk_offset<BN>(n, ks * 2 + hh);
 
   float m_used = -1e30f;   // base of the exponentials (log2 units)
   float m_true = -1e30f;   // exact running row max (log2 units)
@@ -457,7 +448,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   // Mask, row max and (rarely) the move of the exponent base; returns the base.
   // Element i of block kb holds key t0 + kb*32 + (i/4)*8 + hh*4 + i%4.
   auto prep = [&](f32x16 (&s)[NKB], int t0) -> float {
-    const bool need_mask = (a.causal && t0 + KW - 1 > wave_first_qpos) || (t0 + KW > kv_len) ||
+    const bool need_mask = (a.causal && t0 + BN - 1 > wave_first_qpos) || (t0 + BN > kv_len) ||
                            (a.window > 0 && t0 <= wave_first_qpos + 31 - a.window);
     if (need_mask) {
       // visible: lo <= key offset <= hi, offsets relative to t0 + hh*4
@@ -537,7 +528,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     auto iter = [&](int t, auto parity, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
       constexpr int P = decltype(parity)::value;
       if (t + 2 < ntiles) issue_k(t + 2, KST[P]);
-      const float base = prep(cur, (tb + t) * BN + kh * KW);
+      const float base = prep(cur, (tb + t) * BN);
       u32x4 pk[NKS];
       if (t + 1 < ntiles) {
         qk(lds + KST[1 - P], nxt);
@@ -597,7 +588,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
           if (i + AHEAD < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
       }
-      const float base = prep(sc, (tb + t) * BN + kh * KW);
+      const float base = prep(sc, (tb + t) * BN);
       u32x4 pk[NKS];
       expo(sc, base, pk);
       pv(lds + ST_[ST] + KT, pk);
@@ -623,43 +614,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     }
   }
 
-  float lt;
-  if constexpr (KS == 2) {
-    // Merge the two key halves of every query row. Both waves of a pair publish
-    // (m_used, m_true, l); both compute the common base; wave w+4 writes its O
-    // referred to that base, wave w adds it and finishes the row.
-    xs[((kh * 4 + qw) * 3 + 0) * 64 + lane] = m_used;
-    xs[((kh * 4 + qw) * 3 + 1) * 64 + lane] = m_true;
-    xs[((kh * 4 + qw) * 3 + 2) * 64 + lane] = l;
-    __syncthreads();
-    const int partner = (1 - kh) * 4 + qw;
-    const float mu_o = xs[(partner * 3 + 0) * 64 + lane];
-    const float mt_o = xs[(partner * 3 + 1) * 64 + lane];
-    const float l_o = xs[(partner * 3 + 2) * 64 + lane];
-    const float mc = fmaxf(m_used, mu_o);
-    const float f_me = exp2_fast(m_used - mc);
-    float* xo = (float*)lds;                                   // [4 pairs][NDB*16][64 lanes]
-    if (kh == 1) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          xo[((qw * NDB + db) * 16 + i) * 64 + lane] = oacc[db][i] * f_me;
-    }
-    __syncthreads();
-    if (kh == 1) return;
-
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        oacc[db][i] = __builtin_fmaf(oacc[db][i], f_me, xo[((qw * NDB + db) * 16 + i) * 64 + lane]);
-    lt = sum_halves(l * f_me + l_o * exp2_fast(mu_o - mc));
-    m_used = mc;
-    m_true = fmaxf(m_true, mt_o);
-  } else {
-    lt = sum_halves(l);
-  }
+  const float lt = sum_halves(l);
 
   // Refer the outputs back to the true row max: factor = 2^((m_used - kShift) - m_true).
   const float base = m_used - kShift;    // the exponentials (and lt) are relative to 2^base
@@ -693,27 +648,33 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   // Stage this wave's 32 output rows in LDS ([row][D] fp32, 16-byte chunks
   // XOR-swizzled by row), then store whole rows: one store instruction then
   // writes 64 x 16 contiguous bytes instead of 16-byte pieces of 32 rows.
-  constexpr int CPRO = D / 4;                              // 16-byte chunks per O row
+  // At head_dim 256 the rows go out in two halves of 128 dims, so the staging
+  // area stays within the two tile stages (two work-groups per compute unit).
+  // The area is this wave's own: its LDS writes and reads stay in order.
+  constexpr int CPRO = DP / 4;                             // 16-byte chunks per staged row
   constexpr int OSW = CPRO < 32 ? CPRO - 1 : 31;
-  float* stg = (float*)(lds + (KS == 1 ? wave : qw) * OSTG);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int chunk = (db * 32 + g * 8 + hh * 4) / 4;
-      *(f32x4*)(stg + n * D + ((chunk ^ (n & OSW)) << 2)) =
-          f32x4{oacc[db][4 * g] * f, oacc[db][4 * g + 1] * f, oacc[db][4 * g + 2] * f,
-                oacc[db][4 * g + 3] * f};
-    }
+  float* stg = (float*)(lds + wave * OSTG);
   const int row_base = q0 + qw * 32;
   float* obase = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
 #pragma unroll
-  for (int it = 0; it < 32 * CPRO / 64; ++it) {
-    const int idx = it * 64 + lane;
-    const int r = idx / CPRO, c = idx % CPRO;
-    const f32x4 val = *(const f32x4*)(stg + r * D + ((c ^ (r & OSW)) << 2));
-    if (row_base + r < a.seqlen_q)
-      *(f32x4*)(obase + (int64_t)(row_base + r) * a.o_ss + c * 4) = val;
+  for (int part = 0; part < OH; ++part) {
+#pragma unroll
+    for (int db = part * (NDB / OH); db < (part + 1) * (NDB / OH); ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int chunk = (db * 32 - part * DP + g * 8 + hh * 4) / 4;
+        *(f32x4*)(stg + n * DP + ((chunk ^ (n & OSW)) << 2)) =
+            f32x4{oacc[db][4 * g] * f, oacc[db][4 * g + 1] * f, oacc[db][4 * g + 2] * f,
+                  oacc[db][4 * g + 3] * f};
+      }
+#pragma unroll
+    for (int it = 0; it < 32 * CPRO / 64; ++it) {
+      const int idx = it * 64 + lane;
+      const int r = idx / CPRO, c = idx % CPRO;
+      const f32x4 val = *(const f32x4*)(stg + r * DP + ((c ^ (r & OSW)) << 2));
+      if (row_base + r < a.seqlen_q)
+        *(f32x4*)(obase + (int64_t)(row_base + r) * a.o_ss + part * DP + c * 4) = val;
+    }
   }
 }
 
