@@ -22,6 +22,7 @@ throughput on a bounded sample of the prefill workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import statistics
@@ -254,11 +255,47 @@ def cpu_baseline(budget_s=20.0):
             break
         n *= 2
     nrows, dt, flops = last
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{nrows} query rows evenly spaced over the 3314-token prompt, all "
-                      f"{cfg.n_heads_q} heads, fp64 two-pass definition ({flops / 1e9:.2f} "
-                      f"GFLOP in {dt:.2f} s)"}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{nrows} query rows evenly spaced over the 3314-token prompt, all "
+                     f"{cfg.n_heads_q} heads, fp64 two-pass definition ({flops / 1e9:.2f} "
+                     f"GFLOP in {dt:.2f} s)"}
+    try:                                   # the same oracle on one thread, a smaller sample
+        from threadpoolctl import threadpool_limits
+        rows = np.unique(np.linspace(0, cfg.seqlen_q - 1, 128).astype(np.int64))
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=cfg.causal,
+                           dtype=cfg.dtype, rows=rows)
+            dt1 = time.perf_counter() - t0
+        off = cfg.seqlen_kv - cfg.seqlen_q
+        f1 = 4 * cfg.head_dim * cfg.n_heads_q * cfg.batch * int(sum(r + off + 1 for r in rows))
+        out["single_thread"] = {"value": f1 / dt1 / 1e12, "unit": "TFLOP/s",
+                                "sample": f"{len(rows)} query rows, all heads "
+                                          f"({f1 / 1e9:.2f} GFLOP in {dt1:.2f} s)"}
+    except ImportError:
+        pass
+    return out
+
+
+def device_info(torch):
+    """CUs and peak engine clock as the device reports them, and the dense
+    bf16/fp16 MFMA peak they imply (4096 FLOP per clock per CU), next to the
+    datasheet figure the rooflines use."""
+    dev = torch.cuda.current_device()
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+            "mfma_bf16_dense_tflops_datasheet": MI355X_BF16_DENSE_TFLOPS}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, dev) == 0 and khz.value > 0:  # clock, kHz
+            info["peak_clock_mhz"] = khz.value / 1000
+            info["mfma_bf16_dense_tflops_from_device"] = round(
+                props.multi_processor_count * 4096 * khz.value * 1e3 / 1e12, 1)
+    except OSError:
+        pass
+    return info
 
 
 def run_profiling_aid(torch, fa, inputs, args):
@@ -606,6 +643,7 @@ def main():
 
     line["roofline"] = rooflines["prefill_gqa_s3314"]
     line["rooflines"] = rooflines
+    line["device"] = device_info(torch)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline()
