@@ -254,7 +254,8 @@ def test_workspace_size():
     lib = fa.load_library()
     assert lib.fa_prefill_workspace_size(1, 3314, 4, 128) == 1 * 4 * 52 * 64 * 128 * 2
     assert lib.fa_prefill_workspace_size(2, 64, 1, 64) == 2 * 1 * 1 * 64 * 64 * 2
-    assert lib.fa_prefill_workspace_size(1, 100, 2, 256) == 1 * 2 * 2 * 64 * 256 * 2
+    assert lib.fa_prefill_workspace_size(1, 100, 2, 256) == 1 * 2 * 4 * 32 * 256 * 2   # 32-key tiles
+    assert lib.fa_prefill_workspace_size(1, 70, 2, 256) == 1 * 2 * 3 * 32 * 256 * 2
     assert lib.fa_prefill_workspace_size(0, 64, 1, 64) == 0
     assert lib.fa_prefill_workspace_size(1, 100, 2, 512) == 1 * 2 * 4 * 32 * 512 * 2   # 32-key tiles
 
