@@ -445,30 +445,39 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
         s[kb] = mfma_qk<BF16>(
             *(const u32x4*)(kst + ka_off[kk % 8] + (kk / 8) * 256 + kb * 32 * KROW), qr[kk], s[kb]);
   };
-  // Mask, row max and (rarely) the move of the exponent base; returns the base.
+  // Whether a tile straddles a bound of some row of this wave (causal diagonal,
+  // valid length, window edge), i.e. needs the element mask.
+  auto needs_mask = [&](int t0) -> bool {
+    return (a.causal && t0 + BN - 1 > wave_first_qpos) || (t0 + BN > kv_len) ||
+           (a.window > 0 && t0 <= wave_first_qpos + 31 - a.window);
+  };
+  // The element mask of a tile that straddles a bound.
   // Element i of block kb holds key t0 + kb*32 + (i/4)*8 + hh*4 + i%4.
-  auto prep = [&](f32x16 (&s)[NKB], int t0) -> float {
-    const bool need_mask = (a.causal && t0 + BN - 1 > wave_first_qpos) || (t0 + BN > kv_len) ||
-                           (a.window > 0 && t0 <= wave_first_qpos + 31 - a.window);
-    if (need_mask) {
-      // visible: lo <= key offset <= hi, offsets relative to t0 + hh*4
-      const int hi = min(a.causal ? qpos : INT_MAX, kv_len - 1) - t0 - hh * 4;
-      const int lo = a.window > 0 ? qpos - a.window + 1 - t0 - hh * 4 : INT_MIN;
+  auto apply_mask = [&](f32x16 (&s)[NKB], int t0) {
+    // visible: lo <= key offset <= hi, offsets relative to t0 + hh*4
+    const int hi = min(a.causal ? qpos : INT_MAX, kv_len - 1) - t0 - hh * 4;
+    const int lo = a.window > 0 ? qpos - a.window + 1 - t0 - hh * 4 : INT_MIN;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = kb * 32 + (i >> 2) * 8 + (i & 3);
-          if (j > hi || j < lo) s[kb][i] = -INFINITY;
-        }
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int j = kb * 32 + (i >> 2) * 8 + (i & 3);
+        if (j > hi || j < lo) s[kb][i] = -INFINITY;
+      }
+  };
+  // Row max of a (masked) tile, scaled to log2 units: straight-line VALU code
+  // that can be scheduled among MFMAs.
+  auto row_max = [&](const f32x16 (&s)[NKB]) -> float {
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = (kb == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = max_halves(mx);
-    const float tmax = mx * a.scale_log2;   // scale > 0: max commutes with the scaling
+    return mx * a.scale_log2;   // scale > 0: max commutes with the scaling
+  };
+  // The running max and (rarely) the move of the exponent base; returns the base.
+  auto rebase = [&](float tmax) -> float {
     m_true = fmaxf(m_true, tmax);
     const bool grow = tmax > m_used + kSlack;
     if (__ballot(grow)) {
@@ -482,6 +491,10 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
         for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
     }
     return m_used - kShift;
+  };
+  auto prep = [&](f32x16 (&s)[NKB], int t0) -> float {
+    if (needs_mask(t0)) apply_mask(s, t0);
+    return rebase(row_max(s));
   };
   // P = 2^(s*scale*log2e - base) <= 2^(kSlack + kShift) = 32768, packed to fp16.
   auto expo = [&](const f32x16 (&s)[NKB], float base, u32x4 (&pk)[NKS]) {
@@ -517,6 +530,8 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     constexpr unsigned KST[2] = {0, KT};
     constexpr unsigned VST[2] = {2 * KT, 2 * KT + VT};
     f32x16 sa[NKB], sb[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sa[kb] = sb[kb] = f32x16{};   // row_max reads sb once unused
     if (ntiles > 0) { issue_k(0, KST[0]); issue_v(0, VST[0]); }
     if (ntiles > 1) issue_k(1, KST[1]);
     load_q();
@@ -524,11 +539,16 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     __syncthreads();
     if (ntiles > 0) qk(lds + KST[0], sa);
     __syncthreads();   // K(0) is read everywhere before K(2) overwrites it
+    float tm = 0.0f;   // row max of the next tile to exponentiate (log2 units)
+    if (ntiles > 0) {
+      if (needs_mask(tb * BN)) apply_mask(sa, tb * BN);
+      tm = row_max(sa);
+    }
 
     auto iter = [&](int t, auto parity, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
       constexpr int P = decltype(parity)::value;
       if (t + 2 < ntiles) issue_k(t + 2, KST[P]);
-      const float base = prep(cur, (tb + t) * BN);
+      const float base = rebase(tm);
       u32x4 pk[NKS];
       if (t + 1 < ntiles) {
         qk(lds + KST[1 - P], nxt);
@@ -549,15 +569,21 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
       // V(t+1) goes out here rather than with K(t+2): its stage held V(t-1),
       // long consumed, and issuing it mid-tile spreads the DMA over the tile.
       if (t + 1 < ntiles) issue_v(t + 1, VST[1 - P]);
+      // P.V of tile t with the row max of tile t+1 interleaved (its base moves
+      // at the top of the next step, after this P.V, as before); a straddling
+      // tile t+1 is masked first. After the last tile the max is unused.
+      if (t + 1 < ntiles && needs_mask((tb + t + 1) * BN)) apply_mask(nxt, (tb + t + 1) * BN);
       pv(lds + VST[P], pk);
+      tm = row_max(nxt);
       {
-        // P.V: V^T operand reads four MFMAs ahead.
+        // P.V: V^T operand reads four MFMAs ahead; the max's VALU among them.
         constexpr int NP = NKS * NDB, AHEAD = 4;
         __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 1);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
           if (i + AHEAD < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
         }
       }
       dma_wait();        // this wave's part of K(t+2), V(t+1) has landed
