@@ -537,6 +537,18 @@ def main():
                           f"row read once)"}
         del l_partial, l_merge, linfo
         torch.cuda.empty_cache()
+        print("[bench] tiny prefill", file=sys.stderr, flush=True)
+        tcfg = inputs.TINY_CAUSAL          # latency-bound: one work-group, two tiles
+        t_run, t_pack, t_attn = prefill_setup(torch, fa, tcfg)
+        for _ in range(20):
+            t_run()
+        r = time_calls(torch, [t_pack, t_attn], 20)
+        line["prefill_tiny"] = {"workload": tcfg.name,
+                                "us_per_call": round((r[0]["median_ms"] + r[1]["median_ms"]) * 1e3, 2),
+                                "attention_us": round(r[1]["median_ms"] * 1e3, 2),
+                                "v_repack_us": round(r[0]["median_ms"] * 1e3, 2),
+                                "mflop": round(tcfg.flops() / 1e6, 3)}
+        del t_run, t_pack, t_attn
         print("[bench] large-head prefill", file=sys.stderr, flush=True)
 
         hcfg = inputs.LARGE_HEAD
