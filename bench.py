@@ -515,6 +515,25 @@ def main():
             "us_per_call": round(h_ms * 1e3, 1), "partial_us": round(rh[0]["median_ms"] * 1e3, 1),
             "frac_hbm_peak": round(linfo["alg_bytes"] / (h_ms * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4)}
         del h_partial, h_merge
+        # The same lengths at 28/4 heads: seven query heads per wave, Q.K^T on
+        # the matrix cores.
+        gcfg = inputs.LONG_DECODE_G7
+        g_partial, g_merge, ginfo = decode_setup(torch, fa, gcfg)
+        for _ in range(3):
+            g_partial(); g_merge(); ginfo["fused"]()
+        rg = time_calls(torch, [g_partial, g_merge], 20, flush=flush)
+        rgf = time_calls(torch, [ginfo["fused"]], 20, flush=flush)
+        g_ms = rg[0]["median_ms"] + rg[1]["median_ms"]
+        line["decode_batched_long_h28kv4"] = {
+            "workload": gcfg.name, "split_len": ginfo["split_len"],
+            "max_splits": ginfo["max_splits"], "kv_gb": round(ginfo["kv_bytes"] / 1e9, 4),
+            "us_per_call": round(g_ms * 1e3, 1), "partial_us": round(rg[0]["median_ms"] * 1e3, 1),
+            "frac_hbm_peak": round(ginfo["alg_bytes"] / (g_ms * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4),
+            "fused_single_launch_us": round(rgf[0]["median_ms"] * 1e3, 1),
+            "fused_frac_hbm_peak": round(ginfo["alg_bytes"] / (rgf[0]["median_ms"] * 1e-3) / 1e9
+                                         / MI355X_HBM_GBPS, 4),
+            "cache": "flushed (512 MB write) before every call"}
+        del g_partial, g_merge, ginfo
         dk = decode_kernel_name(lcfg)
         rooflines["decode_partial_batched_long"] = {
             "bound": "hbm", "achieved": round(part_gbps, 1), "peak": MI355X_HBM_GBPS,

@@ -142,6 +142,10 @@ GQA_DECODE = DecodeConfig("gqa_decode_b1_h28kv4_d128_kv1641_f16", 1, 28, 4, 128,
                           seed=3, fixed_len=1641)
 LONG_DECODE = DecodeConfig("batched_long_decode_b32_h32kv8_d128_kv512to32768_f16", 32, 32, 8,
                            128, "f16", seed=4, len_range=(512, 32768))
+# The same lengths with the GQA prompt's heads (28 query / 4 KV: seven query
+# heads per wave, the decode form with Q.K^T on the matrix cores).
+LONG_DECODE_G7 = DecodeConfig("batched_long_decode_b32_h28kv4_d128_kv512to32768_f16", 32, 28, 4,
+                              128, "f16", seed=4, len_range=(512, 32768))
 LARGE_HEAD = PrefillConfig("large_head_causal_prefill_b2_h16_d256_s8192_bf16_unnorm", 2, 16, 16,
                            256, 8192, 8192, "bf16", True, seed=5, k_mult=4.0,
                            out_unnormalized=True)
@@ -155,7 +159,8 @@ WINDOW_PREFILL = PrefillConfig("gqa_window1024_causal_prefill_b1_h28kv4_d128_s33
 HD512_PREFILL = PrefillConfig("mqa_hd512_causal_prefill_b1_h16kv1_d512_s4096_bf16", 1, 16, 1,
                               512, 4096, 4096, "bf16", True, seed=7)
 
-WORKLOADS = {c.name: c for c in (TINY_CAUSAL, GQA_PREFILL, GQA_DECODE, LONG_DECODE, LARGE_HEAD,
+WORKLOADS = {c.name: c for c in (TINY_CAUSAL, GQA_PREFILL, GQA_DECODE, LONG_DECODE, LONG_DECODE_G7,
+                                 LARGE_HEAD,
                                  WINDOW_PREFILL, HD512_PREFILL)}
 
 
