@@ -32,7 +32,9 @@
  *     nothing, and leaves a description in fa_last_error(). A failed kernel
  *     launch returns FA_ERR_HIP with the HIP error text.
  *   - Results are deterministic: the same inputs and the same plan give the
- *     same bytes on every run (no atomics; fixed reduction order).
+ *     same bytes on every run (fixed reduction orders; the one atomic, the
+ *     arrival counter of fa_decode_fused, only decides which work-group
+ *     performs the final merge, not its order).
  *   - Thread-safe: no mutable global state besides the per-thread error text.
  */
 #ifndef FA_H
