@@ -84,7 +84,7 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  * combine freely (causal == 0 with a window admits every key after
  * p_i - window). A row that sees no key gets o = 0, row_sum = 0 and
  * lse = -inf. Hidden keys that share a key tile (64 keys; 32 at head_dim
- * 512) with visible ones are read and given weight zero, so K and V must hold
+ * 256 and 512) with visible ones are read and given weight zero, so K and V must hold
  * finite values there too (V within fp16 range; padding past kv_lens[b]
  * included); tiles with no visible key are skipped.
  *
@@ -192,7 +192,7 @@ int fa_attn_merge(const float* o_a, int64_t oa_sb, int64_t oa_ss, int64_t oa_sh,
 /*
  * fa_prefill_workspace_size — bytes of workspace fa_prefill_fwd needs
  * (batch * n_heads_kv * ceil(seqlen_kv / T) * head_dim * T * 2, with tiles of
- * T = 64 keys, 32 at head_dim 512). Returns 0 for non-positive sizes. Host
+ * T = 64 keys, 32 at head_dim 256 and 512). Returns 0 for non-positive sizes. Host
  * only; never fails otherwise.
  */
 uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int head_dim);
