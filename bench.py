@@ -13,9 +13,11 @@ system fence) on the launch stream; the roofline entry uses the attention
 launch alone. The same line carries the
 decode timings, the batched long-context decode (32 sequences, 512..32768
 tokens), the large-head prefill (head_dim 256, 8192 tokens), the GQA prompt
-under a 1024-position sliding window (with and without sinks) and a head_dim
-512 multi-query prefill as extra measurements, a roofline entry per kernel family, and the fp64 CPU oracle's
-throughput on a bounded sample of the prefill workload.
+under a 1024-position sliding window (with and without sinks), a head_dim
+512 multi-query prefill and a long few-head prompt with and without the key
+split of its longest blocks as extra measurements, a roofline entry per kernel
+family, and the fp64 CPU oracle's throughput on a bounded sample of the
+prefill workload.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
@@ -96,9 +98,10 @@ def _events(torch, n):
     return [_HipEvent(torch) for _ in range(n)]
 
 
-def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None):
+def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None, split=False):
     """Prepared (pack, attention) calls for a prefill workload; `tensors`, when
-    a dict, receives the output tensors."""
+    a dict, receives the output tensors. split: the attention call with the key
+    split of the longest query blocks (fa_prefill_fwd_packed_split)."""
     from flashattention_attention_amd import inputs
     x = inputs.make_prefill_inputs(cfg)
     q, k, v = (_dev(torch, x[n], cfg.dtype) for n in ("q", "k", "v"))
@@ -112,10 +115,16 @@ def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None):
 
     # prepared calls: marshalled once, so a launch costs a few microseconds of host
     # time and the host stays ahead of the GPU inside the timed loops
+    sws = None
+    if split:
+        sws = torch.zeros(fa.prefill_split_workspace_size(B, Sq, Hq, D), dtype=torch.uint8,
+                          device="cuda")
+        rs = None   # row sums turn the split off
     pack = fa.prefill_pack_v(v, workspace=ws, prepare=True)
     attn = fa.prefill_packed(q, k, ws, causal=cfg.causal, softmax_scale=cfg.scale,
                              out_unnormalized=cfg.out_unnormalized, out=o, lse=lse, row_sum=rs,
-                             window=cfg.window, sink_logits=sink_logits, prepare=True)
+                             window=cfg.window, sink_logits=sink_logits, split_workspace=sws,
+                             prepare=True)
     if tensors is not None:
         tensors.update(o=o, lse=lse)
 
@@ -125,7 +134,7 @@ def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None):
     return run, pack, attn
 
 
-def prefill_kernel_name(cfg):
+def prefill_kernel_name(cfg, split=False):
     """The attention kernel's template name as rocprofv3 reports it."""
     if cfg.head_dim == 512:
         return (f"prefill512_kernel<{str(cfg.dtype == 'bf16').lower()}, "
@@ -133,7 +142,7 @@ def prefill_kernel_name(cfg):
     group = cfg.n_heads_q // cfg.n_heads_kv
     hp = 2 if cfg.head_dim <= 128 and group % 2 == 0 else 1
     return (f"prefill_kernel<{cfg.head_dim}, {str(cfg.dtype == 'bf16').lower()}, "
-            f"{str(cfg.out_unnormalized).lower()}, {hp}>")
+            f"{str(cfg.out_unnormalized).lower()}, {hp}, {str(split).lower()}>")
 
 
 def decode_kernel_name(cfg):
@@ -306,10 +315,11 @@ def run_profiling_aid(torch, fa, inputs, args):
         dst = torch.empty_like(src)
         fns = [lambda: dst.copy_(src)]
         label = f"copy {args.copy_bytes} bytes"
-    elif args.only in ("prefill", "large_head", "window", "hd512"):
+    elif args.only in ("prefill", "large_head", "window", "hd512", "few_heads_split"):
         cfg = {"prefill": inputs.GQA_PREFILL, "large_head": inputs.LARGE_HEAD,
-               "window": inputs.WINDOW_PREFILL, "hd512": inputs.HD512_PREFILL}[args.only]
-        _, pack, attn = prefill_setup(torch, fa, cfg)
+               "window": inputs.WINDOW_PREFILL, "hd512": inputs.HD512_PREFILL,
+               "few_heads_split": inputs.FEW_HEADS_PREFILL}[args.only]
+        _, pack, attn = prefill_setup(torch, fa, cfg, split=args.only == "few_heads_split")
         fns, label = [pack, attn], cfg.name
     elif args.only == "sink":
         cfg = inputs.WINDOW_PREFILL
@@ -342,7 +352,7 @@ def main():
     ap.add_argument("--split-sweep", action="store_true",
                     help="also time the single-token decode at several split lengths")
     ap.add_argument("--only", choices=["prefill", "decode", "long_decode", "large_head",
-                                              "window", "hd512", "sink"],
+                                              "window", "hd512", "sink", "few_heads_split"],
                     help="profiling aid: run only this component (warmup + steps) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="profiling aid: time a plain device-to-device copy of this many "
@@ -648,6 +658,37 @@ def main():
             "us_per_launch": round(ru[2]["mean_ms"] * 1e3, 1),
             "per_launch": f"{merge_bytes / 1e6:.2f} MB (O and LSE read and written once)"}
         del s_pack, s_attn, p_pack2, p_attn2, s_merge, tens
+        print("[bench] few-heads prefill, unsplit and with the key split", file=sys.stderr,
+              flush=True)
+
+        # One round of very unequal blocks (8 heads x 64 query blocks on 512
+        # slots): the longest blocks' key ranges split over two work-groups.
+        fcfg = inputs.FEW_HEADS_PREFILL
+        units = fa.prefill_split_units(fcfg.batch, fcfg.seqlen_q, fcfg.seqlen_kv, fcfg.n_heads_q,
+                                       fcfg.n_heads_kv, fcfg.head_dim, fcfg.causal, fcfg.window)
+        _, fu_pack, fu_attn = prefill_setup(torch, fa, fcfg)
+        _, fs_pack, fs_attn = prefill_setup(torch, fa, fcfg, split=True)
+        fu_pack(); fu_attn(); fs_pack(); fs_attn()
+        ru = time_calls(torch, [fu_pack, fu_attn], 20)
+        rs = time_calls(torch, [fs_pack, fs_attn], 20)
+        ff = fcfg.flops()
+        fu_tf = ff / (ru[1]["mean_ms"] * 1e-3) / 1e12
+        fs_tf = ff / (rs[1]["mean_ms"] * 1e-3) / 1e12
+        line["prefill_few_heads"] = {
+            "workload": fcfg.name, "split_blocks": sum(1 for _, k in units if k == 1),
+            "blocks": -(-fcfg.seqlen_q // 128),
+            "attention_us_unsplit": round(ru[1]["mean_ms"] * 1e3, 1),
+            "attention_us_split": round(rs[1]["mean_ms"] * 1e3, 1),
+            "tflops_unsplit": round(fu_tf, 2), "tflops_split": round(fs_tf, 2),
+            "v_repack_us": round(rs[0]["mean_ms"] * 1e3, 1)}
+        fk = prefill_kernel_name(fcfg, split=True)
+        rooflines["prefill_few_heads_split"] = {
+            "bound": "mfma", "achieved": round(fs_tf, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(fs_tf / MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": measured_traffic(fk, fcfg.name, "fa_prefill.hip"), "kernel": fk,
+            "us_per_launch": round(rs[1]["mean_ms"] * 1e3, 1),
+            "per_launch": f"{ff / 1e12:.4f} TFLOP"}
+        del fu_pack, fu_attn, fs_pack, fs_attn
         print("[bench] head_dim 512 prefill", file=sys.stderr, flush=True)
 
         xcfg = inputs.HD512_PREFILL

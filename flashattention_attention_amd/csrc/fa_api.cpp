@@ -232,6 +232,68 @@ int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_s
                     "fa_prefill_fwd_packed launch");
 }
 
+int fa_prefill_fwd_packed_split(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                                const void* k, int64_t k_sb, int64_t k_ss, int64_t k_sh,
+                                float* o, int64_t o_sb, int64_t o_ss, int64_t o_sh,
+                                float* lse, float* row_sum,
+                                int batch, int seqlen_q, int seqlen_kv, int n_heads_q,
+                                int n_heads_kv, int head_dim, int dtype, int causal,
+                                float softmax_scale, int out_unnormalized, const int32_t* kv_lens,
+                                int window, const float* sink_logits, const void* workspace,
+                                uint64_t workspace_bytes, void* split_workspace,
+                                uint64_t split_workspace_bytes, void* stream) {
+  const char* fn = "fa_prefill_fwd_packed_split";
+  int st = check_attn(fn, q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, o, o_sb, o_ss, o_sh, lse,
+                      row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, dtype,
+                      softmax_scale, out_unnormalized);
+  if (st == FA_OK) st = check_masks(fn, kv_lens, window, sink_logits);
+  if (st == FA_OK)
+    st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
+  if (st != FA_OK) return st;
+  const fa::SplitLayout L = fa::prefill_split_layout(batch, seqlen_q, n_heads_q, head_dim);
+  if (!split_workspace || split_workspace_bytes < L.total || ((uintptr_t)split_workspace & 255u))
+    return fail(FA_ERR_INVALID_ARG,
+                "%s: split workspace must be 256-byte aligned and hold %llu bytes", fn,
+                (unsigned long long)L.total);
+  const fa::PrefillArgs a =
+      prefill_args(q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, nullptr, 0, 0, 0, o, o_sb, o_ss,
+                   o_sh, lse, row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, causal,
+                   softmax_scale, kv_lens, window, sink_logits);
+  const fa::VtArgs w{const_cast<void*>(workspace), (size_t)workspace_bytes};
+  fa::SplitPlan sp{};
+  if (!out_unnormalized && !row_sum)
+    sp.n_units = fa::prefill_split_units(batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv,
+                                         head_dim, causal, window, sp.units);
+  if (sp.n_units == 0)
+    return hip_status(fa::launch_prefill_attn(a, w, head_dim, dtype == FA_BF16,
+                                              out_unnormalized != 0, (hipStream_t)stream),
+                      "fa_prefill_fwd_packed_split launch");
+  char* ws = (char*)split_workspace;
+  sp.cnt = (int*)(ws + L.cnt);
+  sp.lse = (float*)(ws + L.lse);
+  sp.o = (float*)(ws + L.o);
+  return hip_status(fa::launch_prefill_attn_split(a, w, sp, head_dim, dtype == FA_BF16,
+                                                  (hipStream_t)stream),
+                    "fa_prefill_fwd_packed_split launch");
+}
+
+uint64_t fa_prefill_split_workspace_size(int batch, int seqlen_q, int n_heads_q, int head_dim) {
+  return fa::prefill_split_layout(batch, seqlen_q, n_heads_q, head_dim).total;
+}
+
+int fa_prefill_split_units(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                           int head_dim, int causal, int window, uint16_t* units, int max_units) {
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_kv <= 0 || n_heads_q <= 0 || n_heads_kv <= 0 ||
+      n_heads_q % n_heads_kv != 0 || window < 0 || max_units < 0)
+    return -fail(FA_ERR_INVALID_ARG, "fa_prefill_split_units: invalid sizes");
+  unsigned short tab[fa::kMaxSplitUnits];
+  const int n = fa::prefill_split_units(batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv,
+                                        head_dim, causal, window, tab);
+  if (units)
+    for (int i = 0; i < n && i < max_units; ++i) units[i] = tab[i];
+  return n;
+}
+
 int fa_attn_merge(const float* o_a, int64_t oa_sb, int64_t oa_ss, int64_t oa_sh,
                   const float* lse_a, const float* o_b, int64_t ob_sb, int64_t ob_ss,
                   int64_t ob_sh, const float* lse_b, const float* sink_logits, int batch,

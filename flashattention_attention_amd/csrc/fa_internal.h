@@ -79,6 +79,30 @@ struct VtArgs {
 // Bytes of prefill workspace needed for these sizes.
 size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int head_dim);
 
+// Key split of the longest query blocks of a prefill (normalized output, head
+// dim 64 or 128): the order in which a launch hands out its work units, and
+// the caller's scratch for the halves' partial results. A unit is a whole
+// 128-row query block or one half of a split block's key tiles; unit entry =
+// query block | kind << 14 (kind 0: whole block, 1: first half, 2: second).
+constexpr int kMaxSplitUnits = 512;
+struct SplitPlan {
+  int* cnt;      // [batch * n_heads_q * nqb] arrival counters, zero between calls
+  float* o;      // [batch * n_heads_q * nqb][2 halves][128 rows * head_dim] partial O
+  float* lse;    // [batch * n_heads_q * nqb][2 halves][128 rows] partial LSE (log2 units)
+  int n_units;   // 0: no split (one work-group per block, longest first)
+  unsigned short units[kMaxSplitUnits];   // longest unit first
+};
+// Scratch bytes of the split for these sizes, and the offsets of its parts.
+struct SplitLayout {
+  size_t cnt, lse, o, total;
+};
+SplitLayout prefill_split_layout(int batch, int seqlen_q, int n_heads_q, int head_dim);
+// The work order for one call's shape (kv_lens are not known on the host: full
+// lengths are assumed, which affects only the balance). Returns the unit count
+// (0: the call runs unsplit) and fills units[0 .. count).
+int prefill_split_units(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                        int head_dim, int causal, int window, unsigned short* units);
+
 // Launchers: enqueue on `stream`, return the launch's hipError_t.
 // Prefill in two launches: V -> fp16 V^T tiles in the workspace (uses a.v and
 // its strides), then attention reading the V^T tiles from the workspace.
@@ -86,6 +110,9 @@ hipError_t launch_prefill_pack(const PrefillArgs& a, const VtArgs& w, int head_d
                                hipStream_t stream);
 hipError_t launch_prefill_attn(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
                                bool unnormalized, hipStream_t stream);
+// The same with the key split (sp.n_units > 0); head_dim 64 or 128, normalized output.
+hipError_t launch_prefill_attn_split(const PrefillArgs& a, const VtArgs& w, const SplitPlan& sp,
+                                     int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                                  hipStream_t stream);
 hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

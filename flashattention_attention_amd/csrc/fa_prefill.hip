@@ -57,7 +57,12 @@
 
 #include <limits.h>
 
+#include <algorithm>
+#include <functional>
+#include <mutex>
+#include <queue>
 #include <type_traits>
+#include <vector>
 
 namespace fa {
 namespace {
@@ -277,9 +282,18 @@ __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int
 // ---------------------------------------------------------------------------
 // Attention forward.
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, bool UNNORM, int HP>
+// SPLIT: the work-group runs one unit of the key-split work order (sp): a whole
+// query block, or the first or second half of a long block's key tiles. A
+// half leaves its normalized partial O and LSE in the caller's scratch and the
+// second half to finish merges the two (below, after the tile loop).
+struct NoSplit {};
+template <bool SPLIT> struct SplitArg { using type = NoSplit; };
+template <> struct SplitArg<true> { using type = SplitPlan; };
+
+template <int D, bool BF16, bool UNNORM, int HP, bool SPLIT>
 __global__ void __launch_bounds__(64 * wg_waves(D, HP)) __attribute__((amdgpu_waves_per_eu(2, 2)))
-prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
+prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
+               typename SplitArg<SPLIT>::type sp) {
   constexpr int kWaves = wg_waves(D, HP);
   constexpr bool PIPE = D <= 128;            // software-pipelined loop (register budget)
   constexpr int QG = 4;                      // query groups of 32 rows per head
@@ -316,9 +330,17 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   const int hp = wave / QG;               // which query head of the work-group
   const int nqb = (a.seqlen_q + kBM - 1) / kBM;
   const int per_group = a.n_heads_q / a.n_heads_kv;
-  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nqb);
+  int nunits = nqb;
+  if constexpr (SPLIT) nunits = sp.n_units;
+  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nunits);
   if (!item.valid) return;
-  const int qb = item.qb, b = item.b, hk = item.hk;
+  int qb = item.qb, half = -1;   // half: -1 whole block, else which half of its key tiles
+  if constexpr (SPLIT) {
+    const unsigned e = sp.units[nunits - 1 - item.qb];   // the unit of this rank
+    qb = (int)(e & 0x3fffu);
+    half = (int)(e >> 14) - 1;
+  }
+  const int b = item.b, hk = item.hk;
   const int h = hk * per_group + item.unit * HP + hp;   // the launcher picks HP | per_group
   const int q0 = qb * kBM;
   const int off = a.seqlen_kv - a.seqlen_q;              // bottom-right alignment
@@ -354,8 +376,17 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   int kv_end = kv_len;
   if (a.causal) kv_end = min(kv_end, min(q0 + kBM, a.seqlen_q) + off);
   const int kv_lo = a.window > 0 ? max(0, q0 + off - a.window + 1) : 0;
-  const int tb = kv_lo / BN;
-  const int ntiles = kv_end > kv_lo ? (kv_end + BN - 1) / BN - tb : 0;
+  int tb = kv_lo / BN;
+  int ntiles = kv_end > kv_lo ? (kv_end + BN - 1) / BN - tb : 0;
+  if (SPLIT && half >= 0) {    // first half: tiles [0, n/2); second: [n/2, n)
+    const int n0 = ntiles / 2;
+    if (half == 0) {
+      ntiles = n0;
+    } else {
+      tb += n0;
+      ntiles -= n0;
+    }
+  }
   const int ntiles_all = (a.seqlen_kv + BN - 1) / BN;
   const int wave_first_qpos = q0 + qw * 32 + off;
 
@@ -645,7 +676,80 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   // Refer the outputs back to the true row max: factor = 2^((m_used - kShift) - m_true).
   const float base = m_used - kShift;    // the exponentials (and lt) are relative to 2^base
   float f, lse2, rsum;
-  if (!a.sink_logits) {
+  bool merged = false;
+  if constexpr (SPLIT) {
+    static_assert(!UNNORM, "the key split merges normalized halves");
+    __shared__ int split_last;
+    if (half >= 0) {
+      // This half's normalized partial, O_h = oacc / lt and LSE_h = base +
+      // log2(lt) in log2 units (O_h = 0 and LSE_h = -inf for a row the half
+      // sees no key of). Stored lane-ordered, element e of lane L of a wave at
+      // e * 64 + L of the wave's 32 x D area, with agent-scope stores; the
+      // second half to finish reads the other one back after the counter.
+      const float fp = lt > 0.0f ? 1.0f / lt : 0.0f;
+      const float lp = lt > 0.0f ? base + __log2f(lt) : -INFINITY;
+      const int64_t blk = ((int64_t)b * a.n_heads_q + h) * nqb + qb;
+      float* po = sp.o + ((blk * 2 + half) * kBM + qw * 32) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          __hip_atomic_store(po + (db * 16 + i) * 64 + lane, oacc[db][i] * fp, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      if (hh == 0)
+        __hip_atomic_store(sp.lse + (blk * 2 + half) * kBM + qw * 32 + n, lp, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      // Count this half once its partial has reached memory; the second merges.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        split_last = __hip_atomic_fetch_add(sp.cnt + blk, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == 1;
+      __syncthreads();
+      if (!split_last) return;
+      // The other half's partial, read with agent-scope loads: an agent-scope
+      // acquire fence would invalidate this XCD's whole L2, and with it the
+      // K / V^T tiles the other work-groups on the XCD are streaming.
+      const float* qo = sp.o + ((blk * 2 + (1 - half)) * kBM + qw * 32) * D;
+      const float lo = __hip_atomic_load(sp.lse + (blk * 2 + (1 - half)) * kBM + qw * 32 + n,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // Merge with the first half always as the left operand, so the result
+      // does not depend on which half finished last.
+      const float la = half == 0 ? lp : lo, lb = half == 0 ? lo : lp;
+      const float mm = fmaxf(la, lb);
+      const float wa = mm == -INFINITY ? 0.0f : exp2_fast(la - mm);
+      const float wb = mm == -INFINITY ? 0.0f : exp2_fast(lb - mm);
+      const float ws = wa + wb;     // sum of the row's key terms relative to 2^mm
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float mine = oacc[db][i] * fp;
+          const float other = __hip_atomic_load(qo + (db * 16 + i) * 64 + lane,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const float xa = half == 0 ? mine : other, xb = half == 0 ? other : mine;
+          oacc[db][i] = wa * xa + wb * xb;
+        }
+      if (!a.sink_logits) {
+        lse2 = ws > 0.0f ? mm + __log2f(ws) : -INFINITY;
+        f = ws > 0.0f ? 1.0f / ws : 0.0f;
+      } else {
+        // the sink as one more term 2^sg, as in the unsplit case below
+        const float sg = a.sink_logits[h] * kLog2e;
+        const float lns = ws > 0.0f ? mm + __log2f(ws) : -INFINITY;
+        const float mx = fmaxf(lns, sg);
+        lse2 = mx == -INFINITY ? -INFINITY
+                               : mx + __log2f(exp2_fast(lns - mx) + exp2_fast(sg - mx));
+        f = ws > 0.0f ? exp2_fast(mm - lse2) : 0.0f;
+      }
+      rsum = 0.0f;   // the split is not used when row sums are requested
+      if (tid == 0) __hip_atomic_store(sp.cnt + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merged = true;
+    }
+  }
+  if (merged) {
+    // f and lse2 come from the merge of the two halves above
+  } else if (!a.sink_logits) {
     const float to_true = exp2_fast(base - m_true);
     // a row with no visible key (length or window mask) has lt = 0: O = 0, LSE = -inf
     f = UNNORM ? to_true : (lt > 0.0f ? 1.0f / lt : 0.0f);
@@ -989,11 +1093,33 @@ hipError_t launch_attn_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hip
     constexpr int HP = decltype(hp_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
     if (unnorm)
-      hipLaunchKernelGGL((prefill_kernel<D, BF16, true, HP>), grid, dim3(64 * wg_waves(D, HP)), 0,
-                         stream, a, (const unsigned short*)w.ws);
+      hipLaunchKernelGGL((prefill_kernel<D, BF16, true, HP, false>), grid,
+                         dim3(64 * wg_waves(D, HP)), 0, stream, a, (const unsigned short*)w.ws,
+                         NoSplit{});
     else
-      hipLaunchKernelGGL((prefill_kernel<D, BF16, false, HP>), grid, dim3(64 * wg_waves(D, HP)),
-                         0, stream, a, (const unsigned short*)w.ws);
+      hipLaunchKernelGGL((prefill_kernel<D, BF16, false, HP, false>), grid,
+                         dim3(64 * wg_waves(D, HP)), 0, stream, a, (const unsigned short*)w.ws,
+                         NoSplit{});
+  };
+  if constexpr (D <= 128) {
+    if (per_group % 2 == 0) {
+      go(std::integral_constant<int, 2>{});
+      return hipGetLastError();
+    }
+  }
+  go(std::integral_constant<int, 1>{});
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_split_d(const PrefillArgs& a, const VtArgs& w, const SplitPlan& sp,
+                          hipStream_t stream) {
+  const int per_group = a.n_heads_q / a.n_heads_kv;
+  const auto go = [&](auto hp_c) {
+    constexpr int HP = decltype(hp_c)::value;
+    const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, sp.n_units));
+    hipLaunchKernelGGL((prefill_kernel<D, BF16, false, HP, true>), grid,
+                       dim3(64 * wg_waves(D, HP)), 0, stream, a, (const unsigned short*)w.ws, sp);
   };
   if constexpr (D <= 128) {
     if (per_group % 2 == 0) {
@@ -1025,6 +1151,176 @@ size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int hea
   const size_t bn = tile_keys(head_dim);
   const size_t ntiles = ((size_t)seqlen_kv + bn - 1) / bn;
   return (size_t)batch * n_heads_kv * ntiles * bn * head_dim * 2;
+}
+
+SplitLayout prefill_split_layout(int batch, int seqlen_q, int n_heads_q, int head_dim) {
+  SplitLayout L{};
+  if (batch <= 0 || seqlen_q <= 0 || n_heads_q <= 0 || head_dim <= 0) return L;
+  const size_t blocks = (size_t)batch * n_heads_q * (((size_t)seqlen_q + 127) / 128);
+  const auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  L.cnt = 0;
+  L.lse = up(blocks * 4);
+  L.o = L.lse + up(blocks * 2 * 128 * 4);
+  L.total = L.o + blocks * 2 * 128 * (size_t)head_dim * 4;
+  return L;
+}
+
+namespace {
+
+// End time of handing out the units in list order, `copies` work-groups per
+// unit, each to the earliest free of `slots` work-group slots (time in tiles).
+double list_makespan(const std::vector<double>& sizes, int64_t copies, int slots) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> q;
+  for (int i = 0; i < slots; ++i) q.push(0.0);
+  double end = 0.0;
+  for (const double u : sizes)
+    for (int64_t c = 0; c < copies; ++c) {
+      const double t = q.top() + u;
+      q.pop();
+      q.push(t);
+      end = std::max(end, t);
+    }
+  return end;
+}
+
+struct PlanKey {
+  int batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, causal, window;
+  bool operator==(const PlanKey& o) const {
+    return batch == o.batch && seqlen_q == o.seqlen_q && seqlen_kv == o.seqlen_kv &&
+           n_heads_q == o.n_heads_q && n_heads_kv == o.n_heads_kv && head_dim == o.head_dim &&
+           causal == o.causal && window == o.window;
+  }
+};
+struct PlanEntry {
+  PlanKey key;
+  int n_units;
+  std::vector<unsigned short> units;
+};
+
+int plan_units(const PlanKey& k, unsigned short* units) {
+  const int D = k.head_dim;
+  if (D != 64 && D != 128) return 0;
+  const int bm = 128, bn = tile_keys(D);
+  const int nqb = (k.seqlen_q + bm - 1) / bm;
+  if (nqb <= 0 || nqb > 0x3fff) return 0;
+  // key tiles per query block, as the kernel counts them at full lengths
+  const int off = k.seqlen_kv - k.seqlen_q;
+  std::vector<int> tiles(nqb);
+  for (int qb = 0; qb < nqb; ++qb) {
+    const int q0 = qb * bm;
+    int kv_end = k.seqlen_kv;
+    if (k.causal) kv_end = std::min(kv_end, std::min(q0 + bm, k.seqlen_q) + off);
+    const int kv_lo = k.window > 0 ? std::max(0, q0 + off - k.window + 1) : 0;
+    tiles[qb] = kv_end > kv_lo ? (kv_end + bn - 1) / bn - kv_lo / bn : 0;
+  }
+  const int per_group = k.n_heads_q / k.n_heads_kv;
+  const int hp = (D <= 128 && per_group % 2 == 0) ? 2 : 1;
+  const int slots = kDecodeCus * 8 / wg_waves(D, hp);          // two waves per SIMD
+  const int64_t copies = (int64_t)k.batch * k.n_heads_kv * (per_group / hp);
+  // What a half costs beyond its tiles, in tile times: its own prologue (Q and
+  // the first tiles in flight), storing its partial, the counter and the
+  // merge. Fitted to measured split / unsplit times of the causal and the
+  // windowed 3314-token prompt (the model ignores that a work-group alone on
+  // its compute unit runs faster, so it overstates the tail it removes).
+  constexpr double kHalfCost = 6.0;
+
+  // Candidate: split every block of more than `thr` tiles; units longest first
+  // (a half's length includes its extra cost).
+  struct Unit { double size; unsigned short e; };
+  const auto build = [&](int thr, std::vector<Unit>& list) {
+    list.clear();
+    for (int qb = nqb - 1; qb >= 0; --qb) {
+      const int n = tiles[qb];
+      if (n > thr && n >= 2) {
+        list.push_back({n / 2 + kHalfCost, (unsigned short)(qb | 1 << 14)});
+        list.push_back({n - n / 2 + kHalfCost, (unsigned short)(qb | 2 << 14)});
+      } else {
+        list.push_back({(double)n, (unsigned short)qb});
+      }
+    }
+    std::stable_sort(list.begin(), list.end(),
+                     [](const Unit& x, const Unit& y) { return x.size > y.size; });
+  };
+  const auto cost = [&](const std::vector<Unit>& list) {
+    std::vector<double> sz;
+    sz.reserve(list.size());
+    for (const Unit& u : list) sz.push_back(u.size);
+    return list_makespan(sz, copies, slots);
+  };
+  std::vector<Unit> list, best;
+  build(INT_MAX, list);
+  const double none = cost(list);
+  // Only a launch whose longest blocks far outlast the average slot's work is
+  // worth splitting: one round of very unequal blocks (few heads, a long
+  // prompt). Measured: 8 heads x 8192 tokens gains 12 % (modeled end 2.0x the
+  // average); the 28-head 3314-token prompt (1.35x) lost 6 % with its three
+  // longest blocks split, since a work-group alone on its compute unit runs
+  // ~1.7x faster and the tail costs less than the model says.
+  double total = 0.0;
+  for (const Unit& u : list) total += u.size;
+  if (none < 1.5 * total * copies / slots) return 0;
+  double best_cost = none;
+  std::vector<int> cands(tiles);
+  std::sort(cands.begin(), cands.end());
+  cands.erase(std::unique(cands.begin(), cands.end()), cands.end());
+  for (const int thr : cands) {
+    build(thr, list);
+    if ((int)list.size() > kMaxSplitUnits || (int)list.size() == nqb) continue;
+    const double c = cost(list);
+    if (c < best_cost) {
+      best_cost = c;
+      best = list;
+    }
+  }
+  if (best.empty() || best_cost > 0.95 * none) return 0;
+  for (size_t i = 0; i < best.size(); ++i) units[i] = best[i].e;
+  return (int)best.size();
+}
+
+}  // namespace
+
+int prefill_split_units(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                        int head_dim, int causal, int window, unsigned short* units) {
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_kv <= 0 || n_heads_q <= 0 || n_heads_kv <= 0 ||
+      n_heads_q % n_heads_kv != 0)
+    return 0;
+  const PlanKey key{batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, causal != 0,
+                    window > 0 ? window : 0};
+  // The plan is a pure function of the shape; the last few are kept.
+  static std::mutex mu;
+  static PlanEntry cache[8];
+  static int filled = 0, next = 0;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (int i = 0; i < filled; ++i)
+      if (cache[i].key == key) {
+        std::copy(cache[i].units.begin(), cache[i].units.end(), units);
+        return cache[i].n_units;
+      }
+  }
+  const int n = plan_units(key, units);
+  std::lock_guard<std::mutex> g(mu);
+  PlanEntry& e = cache[next];
+  e.key = key;
+  e.n_units = n;
+  e.units.assign(units, units + n);
+  next = (next + 1) % 8;
+  filled = std::min(filled + 1, 8);
+  return n;
+}
+
+hipError_t launch_prefill_attn_split(const PrefillArgs& a, const VtArgs& w, const SplitPlan& sp,
+                                     int head_dim, bool bf16, hipStream_t stream) {
+  switch (head_dim) {
+    case 64:
+      return bf16 ? launch_split_d<64, true>(a, w, sp, stream)
+                  : launch_split_d<64, false>(a, w, sp, stream);
+    case 128:
+      return bf16 ? launch_split_d<128, true>(a, w, sp, stream)
+                  : launch_split_d<128, false>(a, w, sp, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_prefill_pack(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,

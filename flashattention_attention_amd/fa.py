@@ -36,6 +36,14 @@ _SIGNATURES = {
                                _vp, _i64, _i64, _i64, _vp, _vp,
                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                _vp, _i32, _vp, _vp, ctypes.c_uint64, _vp], _i32),
+    "fa_prefill_fwd_packed_split": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                                     _vp, _i64, _i64, _i64, _vp, _vp,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                     _vp, _i32, _vp, _vp, ctypes.c_uint64, _vp, ctypes.c_uint64,
+                                     _vp], _i32),
+    "fa_prefill_split_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
+    "fa_prefill_split_units": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                ctypes.POINTER(ctypes.c_uint16), _i32], _i32),
     "fa_attn_merge": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                        _i32, _i32, _i32, _i32, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "fa_prefill_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
@@ -282,9 +290,13 @@ def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
                    lse: Optional[torch.Tensor] = None, row_sum: Optional[torch.Tensor] = None,
                    want_row_sum: bool = False, kv_lens: Optional[torch.Tensor] = None,
                    window: int = 0, sink_logits: Optional[torch.Tensor] = None,
-                   prepare: bool = False):
+                   split_workspace: Optional[torch.Tensor] = None, prepare: bool = False):
     """prefill() with V taken from a workspace filled by prefill_pack_v (same shapes).
-    With prepare=True, returns a callable that repeats the call (pass the outputs)."""
+    With split_workspace (a zero-filled uint8 GPU tensor of at least
+    prefill_split_workspace_size(...) bytes, reusable across calls), the key
+    ranges of the longest query blocks are split over two work-groups
+    (fa_prefill_fwd_packed_split). With prepare=True, returns a callable that
+    repeats the call (pass the outputs)."""
     dev = _on_gpu(q, k, packed_v)
     out, lse, row_sum, need_rs = _prefill_outputs(q, k, dev, out, lse, row_sum,
                                                   out_unnormalized, want_row_sum)
@@ -293,15 +305,22 @@ def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
     kv_lens, window = _masks(kv_lens, window, B, dev)
     sink_logits = _sinks(sink_logits, Hq, dev)
-    call = _issue("fa_prefill_fwd_packed", (
-        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
-        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
-        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
-        lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
-        B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
-        1 if out_unnormalized else 0, _ptr(kv_lens), window, _ptr(sink_logits),
-        packed_v.data_ptr(), packed_v.numel() * packed_v.element_size(), _stream(dev)),
-        (q, k, packed_v, out, lse, row_sum, kv_lens, sink_logits), prepare)
+    args = (q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+            k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+            out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+            lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
+            B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
+            1 if out_unnormalized else 0, _ptr(kv_lens), window, _ptr(sink_logits),
+            packed_v.data_ptr(), packed_v.numel() * packed_v.element_size())
+    keep = (q, k, packed_v, out, lse, row_sum, kv_lens, sink_logits)
+    if split_workspace is None:
+        call = _issue("fa_prefill_fwd_packed", args + (_stream(dev),), keep, prepare)
+    else:
+        _on_gpu(split_workspace)
+        call = _issue("fa_prefill_fwd_packed_split",
+                      args + (split_workspace.data_ptr(),
+                              split_workspace.numel() * split_workspace.element_size(),
+                              _stream(dev)), keep + (split_workspace,), prepare)
     if prepare:
         return call
     return (out, lse, row_sum) if need_rs else (out, lse)
@@ -360,6 +379,27 @@ def attn_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: Optional[torch.Tenso
 def prefill_workspace_size(batch: int, seqlen_kv: int, n_heads_kv: int, head_dim: int) -> int:
     """Bytes of workspace fa_prefill_fwd needs for these sizes."""
     return int(load_library().fa_prefill_workspace_size(batch, seqlen_kv, n_heads_kv, head_dim))
+
+
+def prefill_split_workspace_size(batch: int, seqlen_q: int, n_heads_q: int,
+                                 head_dim: int) -> int:
+    """Bytes of (zero-filled) split workspace fa_prefill_fwd_packed_split needs."""
+    return int(load_library().fa_prefill_split_workspace_size(batch, seqlen_q, n_heads_q,
+                                                              head_dim))
+
+
+def prefill_split_units(batch: int, seqlen_q: int, seqlen_kv: int, n_heads_q: int,
+                        n_heads_kv: int, head_dim: int, causal: bool = True,
+                        window: int = 0) -> list:
+    """The split prefill's work order for a shape (host only): a list of
+    (query block, kind) longest first, kind 0 = whole block, 1 / 2 = first /
+    second half of its key tiles; empty when the call runs unsplit."""
+    lib = load_library()
+    buf = (ctypes.c_uint16 * 512)()
+    n = lib.fa_prefill_split_units(batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim,
+                                   1 if causal else 0, window, buf, 512)
+    _check(-n if n < 0 else 0, "fa_prefill_split_units")
+    return [(buf[i] & 0x3FFF, buf[i] >> 14) for i in range(n)]
 
 
 def decode_plan(kv_lens: Sequence[int], n_heads_q: int, n_heads_kv: int, head_dim: int,

@@ -159,9 +159,15 @@ WINDOW_PREFILL = PrefillConfig("gqa_window1024_causal_prefill_b1_h28kv4_d128_s33
 HD512_PREFILL = PrefillConfig("mqa_hd512_causal_prefill_b1_h16kv1_d512_s4096_bf16", 1, 16, 1,
                               512, 4096, 4096, "bf16", True, seed=7)
 
+# A long causal prompt over few heads (8 query heads, one per KV head): 64
+# query blocks x 8 heads fill 512 work-group slots once, so the launch runs as
+# long as its longest block (128 key tiles) unless long blocks are split.
+FEW_HEADS_PREFILL = PrefillConfig("few_heads_causal_prefill_b1_h8_d128_s8192_bf16", 1, 8, 8, 128,
+                                  8192, 8192, "bf16", True, seed=7)
+
 WORKLOADS = {c.name: c for c in (TINY_CAUSAL, GQA_PREFILL, GQA_DECODE, LONG_DECODE, LONG_DECODE_G7,
                                  LARGE_HEAD,
-                                 WINDOW_PREFILL, HD512_PREFILL)}
+                                 WINDOW_PREFILL, HD512_PREFILL, FEW_HEADS_PREFILL)}
 
 
 def make_prefill_inputs(cfg: PrefillConfig, seed: Optional[int] = None) -> dict:

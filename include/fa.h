@@ -163,6 +163,85 @@ int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_s
                           uint64_t workspace_bytes, void* stream);
 
 /*
+ * fa_prefill_fwd_packed_split — fa_prefill_fwd_packed with the key range of
+ * the longest query blocks split over two work-groups.
+ *
+ * Source: as fa_prefill_fwd_packed; "66 · D2 ...", section 1 (splitting the
+ * KV range of one query into parts whose partial results are merged, with
+ * the partition a fixed function of the shape) and "STAGE_D.md ...", D5 and
+ * D5c (partials carry an LSE and are merged inside the one launch).
+ *
+ * Same arguments, checks and results as fa_prefill_fwd_packed, plus
+ * split_workspace: caller-owned device scratch of at least
+ * fa_prefill_split_workspace_size(batch, seqlen_q, n_heads_q, head_dim)
+ * bytes, 256-byte aligned, zero-filled before its first use; every call
+ * leaves the arrival counters it uses at zero again, so one fill serves
+ * any number of later calls. Calls that overlap in time must not share it.
+ *
+ * Under causal masks (and windows) the 128-row query blocks see different
+ * numbers of key tiles, and a launch cannot end before its longest block
+ * does. The host plans, from the shape alone, which blocks to split
+ * (fa_prefill_split_units): a split block's tiles go to two work-groups,
+ * each stores its normalized partial O and LSE in split_workspace, and the
+ * second to finish merges the two (max-shifted weights, first half always
+ * the left operand), so results are the same bytes on every run. The
+ * partition of the key range changes the float summation order: results
+ * differ from fa_prefill_fwd_packed's within the same tolerances, not
+ * bitwise. With out_unnormalized != 0, a row_sum output, head_dim 256 or
+ * 512, or a shape the planner does not split, the call runs
+ * fa_prefill_fwd_packed's kernel unchanged (split_workspace is then
+ * checked but not touched).
+ */
+int fa_prefill_fwd_packed_split(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                                const void* k, int64_t k_sb, int64_t k_ss, int64_t k_sh,
+                                float* o, int64_t o_sb, int64_t o_ss, int64_t o_sh,
+                                float* lse, float* row_sum,
+                                int batch, int seqlen_q, int seqlen_kv, int n_heads_q,
+                                int n_heads_kv, int head_dim, int dtype, int causal,
+                                float softmax_scale, int out_unnormalized, const int32_t* kv_lens,
+                                int window, const float* sink_logits, const void* workspace,
+                                uint64_t workspace_bytes, void* split_workspace,
+                                uint64_t split_workspace_bytes, void* stream);
+
+/*
+ * fa_prefill_split_workspace_size — bytes of split_workspace
+ * fa_prefill_fwd_packed_split needs: for every 128-row query block of every
+ * (batch entry, query head), a 4-byte counter and two halves of partial
+ * results (128 x head_dim fp32 O and 128 fp32 LSE each), i.e. about
+ * 2 * batch * n_heads_q * ceil(seqlen_q / 128) * 128 * (head_dim + 1) * 4.
+ * Returns 0 for non-positive sizes. Host only; never fails otherwise.
+ */
+uint64_t fa_prefill_split_workspace_size(int batch, int seqlen_q, int n_heads_q, int head_dim);
+
+/*
+ * fa_prefill_split_units — the work order fa_prefill_fwd_packed_split uses
+ * for a shape (host only; for inspection and tests).
+ *
+ * Source: as fa_prefill_fwd_packed_split.
+ *
+ * The plan counts each query block's key tiles at full lengths (kv_lens are
+ * device data; they change only the balance, never the results), models the
+ * launch as list scheduling of work-groups, longest first, on two
+ * work-groups per compute unit of 256 (a half costs 6 tile times beyond its
+ * tiles: its own prologue, storing its partial and the merge), and picks
+ * the split threshold that minimizes the modeled end time. A launch whose
+ * unsplit end is modeled under 1.5x the average slot's work is not split
+ * (a work-group alone on its compute unit runs faster than the model
+ * assumes, so such tails cost less than the split), nor is a plan that
+ * gains under 5 %. In practice: long prompts over few heads split, prompts
+ * over many heads (or batches) do not.
+ * Returns the number of units (0: the call runs unsplit) and writes up to
+ * max_units of them to units (may be NULL), longest first; unit =
+ * query block | kind << 14 with kind 0 = the whole block, 1 = the first
+ * half of its key tiles (floor(n / 2) of n), 2 = the second half. Every block
+ * appears either whole or as both halves. Returns -FA_ERR_INVALID_ARG (a
+ * negative count) for non-positive sizes, bad head counts, window < 0 or
+ * max_units < 0; head dims other than 64 and 128 get 0.
+ */
+int fa_prefill_split_units(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                           int head_dim, int causal, int window, uint16_t* units, int max_units);
+
+/*
  * fa_attn_merge — merge two attention passes over disjoint key sets, and an
  * optional per-head sink, through their LSEs.
  *

@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol():
                           "fa_prefill_workspace_size", "fa_decode_plan",
                           "fa_decode_split_partial", "fa_decode_merge_lse", "fa_decode_fused",
                           "fa_decode_fused_workspace_size", "fa_decode_fused_waves",
-                          "fa_attn_merge",
+                          "fa_attn_merge", "fa_prefill_fwd_packed_split",
+                          "fa_prefill_split_workspace_size", "fa_prefill_split_units",
                           "fa_status_string", "fa_last_error"}
     lib = ctypes.CDLL(fa.library_path())
     for name in names:

@@ -49,9 +49,11 @@ def test_prefill_kernels_run_two_waves_without_scratch():
     rep = _report()
     ks = _pick(rep, "prefill_kernelILi64E", "prefill_kernelILi128E", "prefill_kernelILi256E",
                "prefill512_kernel")
-    # head_dim 64 and 128: {bf16, fp16} x {normalized, un-normalized} x {1, 2 heads};
+    # head_dim 64 and 128: {bf16, fp16} x {normalized, un-normalized} x {1, 2 heads},
+    # plus the key-split form ({bf16, fp16} x {1, 2 heads}, normalized);
     # head_dim 256 and 512: {bf16, fp16} x {normalized, un-normalized}
-    assert len(ks) == 24, sorted(ks)
+    assert len(ks) == 32, sorted(ks)
+    assert len([k for k in ks if "Lb1EEEvNS" in k and "prefill_kernel" in k]) == 8, sorted(ks)
     for name, r in ks.items():
         assert r["scratch_bytes"] == 0 and r["vgpr_spill"] == 0, (name, r)
         assert r["waves_per_simd"] == 2, (name, r)
