@@ -226,7 +226,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
             row_sum: Optional[torch.Tensor] = None, want_row_sum: bool = False,
             workspace: Optional[torch.Tensor] = None, kv_lens: Optional[torch.Tensor] = None,
-            window: int = 0, sink_logits: Optional[torch.Tensor] = None):
+            window: int = 0, sink_logits: Optional[torch.Tensor] = None,
+            split_workspace: Optional[torch.Tensor] = None):
     """Attention forward. q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (fp16/bf16, D contiguous).
 
     ``kv_lens`` (optional int32 GPU tensor [B]) hides keys j >= kv_lens[b];
@@ -237,6 +238,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
 
     ``workspace`` (optional) is a uint8 GPU tensor of at least
     ``prefill_workspace_size(...)`` bytes; one is allocated when omitted.
+    ``split_workspace`` (optional, zero-filled before its first use): run as
+    prefill_pack_v + prefill_packed with the key split of the longest query
+    blocks (see prefill_packed).
 
     Returns (o, lse) or (o, lse, row_sum) when ``out_unnormalized`` or
     ``want_row_sum``; o is fp32 [B,Sq,Hq,D] (un-normalized when asked), lse and
@@ -255,6 +259,13 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
     kv_lens, window = _masks(kv_lens, window, B, dev)
     sink_logits = _sinks(sink_logits, Hq, dev)
     workspace = _workspace(k, dev, workspace)
+    if split_workspace is not None:
+        prefill_pack_v(v, workspace)
+        return prefill_packed(q, k, workspace, causal=causal, softmax_scale=scale,
+                              out_unnormalized=out_unnormalized, out=out, lse=lse,
+                              row_sum=row_sum, want_row_sum=want_row_sum, kv_lens=kv_lens,
+                              window=window, sink_logits=sink_logits,
+                              split_workspace=split_workspace)
     st = load_library().fa_prefill_fwd(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),

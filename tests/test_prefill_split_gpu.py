@@ -138,3 +138,24 @@ def test_split_prefill_full_size(torch_gpu, cfg):
     ref = oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=cfg.causal,
                          dtype=cfg.dtype, rows=rows, window=cfg.window)
     _check(*runs[0], ref, rows=rows)
+
+
+def test_one_call_prefill_with_split_workspace(torch_gpu):
+    """fa.prefill(..., split_workspace=...) runs the V repack and the split
+    attention: the same bytes as the two calls made separately."""
+    from flashattention_attention_amd import fa
+    torch = torch_gpu
+    _say("one-call prefill with split workspace")
+    rng = np.random.default_rng(11)
+    B, S, Hq, Hkv, D, dtype = 1, 1000, 8, 8, 64, "f16"
+    q = _dev(torch, inputs.draw_half(rng, (B, S, Hq, D), dtype), dtype)
+    k = _dev(torch, inputs.draw_half(rng, (B, S, Hkv, D), dtype), dtype)
+    v = _dev(torch, inputs.draw_half(rng, (B, S, Hkv, D), dtype), dtype)
+    assert fa.prefill_split_units(B, S, S, Hq, Hkv, D, True, 0)
+    sws = torch.zeros(fa.prefill_split_workspace_size(B, S, Hq, D), dtype=torch.uint8,
+                      device="cuda")
+    o1, l1 = fa.prefill(q, k, v, split_workspace=sws)
+    o2, l2 = fa.prefill_packed(q, k, fa.prefill_pack_v(v), split_workspace=sws)
+    torch.cuda.synchronize()
+    assert o1.cpu().numpy().tobytes() == o2.cpu().numpy().tobytes()
+    assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes()
