@@ -95,6 +95,8 @@ CASES = [
     # a one-key sequence: the first half of every split block of it sees no key
     ("lens_and_sinks_f16", 3, 900, 900, 8, 4, 128, "f16", True, 0, [900, 451, 1], True, 4.0),
     ("window_sinks_d64", 1, 2500, 2500, 4, 4, 64, "bf16", True, 800, None, True, 1.0),
+    # paired heads, fp16, a sequence shorter than the prompt's blocks reach
+    ("paired_heads_lens_f16", 2, 1400, 1400, 8, 4, 128, "f16", True, 0, [1400, 650], False, 4.0),
 ]
 
 
