@@ -72,7 +72,8 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
     resources = {}
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
-    for src in SOURCES:
+    procs = []
+    for src in SOURCES:   # the sources compile concurrently (one process each)
         obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
         hip = src.endswith(".hip")
         lang = ["-x", "hip"] if hip else []
@@ -80,13 +81,16 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
         cmd = [hipcc()] + compile_flags() + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        procs.append((src, hip, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                      stderr=subprocess.PIPE, text=True)))
+    for src, hip, obj, proc in procs:
+        out, err = proc.communicate()
+        if proc.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{out}\n{err}")
         if hip:
-            resources.update(parse_resource_remarks(r.stderr))
+            resources.update(parse_resource_remarks(err))
         if resource_usage or verbose:
-            sys.stdout.write(r.stderr)
+            sys.stdout.write(err)
         objs.append(obj)
     with open(RESOURCES, "w") as f:
         json.dump(resources, f, indent=1, sort_keys=True)

@@ -85,8 +85,15 @@ size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int hea
 // 128-row query block or one half of a split block's key tiles; unit entry =
 // query block | kind << 14 (kind 0: whole block, 1: first half, 2: second).
 constexpr int kMaxSplitUnits = 512;
+// The arrival counters sit in a fixed region at the start of the split
+// scratch, the same region for every shape: a scratch zero-filled once then
+// serves calls of any shape (each call leaves its counters at zero), and one
+// call's partial results never land on another shape's counters. A shape
+// with more query blocks than counters runs unsplit.
+constexpr size_t kSplitCounterBytes = 65536;
+constexpr int64_t kSplitCounters = (int64_t)(kSplitCounterBytes / 4);
 struct SplitPlan {
-  int* cnt;      // [batch * n_heads_q * nqb] arrival counters, zero between calls
+  int* cnt;      // [batch * n_heads_q * nqb] arrival counters (fixed region), zero between calls
   float* o;      // [batch * n_heads_q * nqb][2 halves][128 rows * head_dim] partial O
   float* lse;    // [batch * n_heads_q * nqb][2 halves][128 rows] partial LSE (log2 units)
   int n_units;   // 0: no split (one work-group per block, longest first)

@@ -1158,8 +1158,8 @@ SplitLayout prefill_split_layout(int batch, int seqlen_q, int n_heads_q, int hea
   if (batch <= 0 || seqlen_q <= 0 || n_heads_q <= 0 || head_dim <= 0) return L;
   const size_t blocks = (size_t)batch * n_heads_q * (((size_t)seqlen_q + 127) / 128);
   const auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  L.cnt = 0;
-  L.lse = up(blocks * 4);
+  L.cnt = 0;                      // fixed for every shape (see kSplitCounterBytes)
+  L.lse = kSplitCounterBytes;
   L.o = L.lse + up(blocks * 2 * 128 * 4);
   L.total = L.o + blocks * 2 * 128 * (size_t)head_dim * 4;
   return L;
@@ -1203,6 +1203,8 @@ int plan_units(const PlanKey& k, unsigned short* units) {
   const int bm = 128, bn = tile_keys(D);
   const int nqb = (k.seqlen_q + bm - 1) / bm;
   if (nqb <= 0 || nqb > 0x3fff) return 0;
+  // one arrival counter per query block of every (batch entry, query head)
+  if ((int64_t)k.batch * k.n_heads_q * nqb > kSplitCounters) return 0;
   // key tiles per query block, as the kernel counts them at full lengths
   const int off = k.seqlen_kv - k.seqlen_q;
   std::vector<int> tiles(nqb);

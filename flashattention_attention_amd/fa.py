@@ -304,7 +304,8 @@ def prefill_packed(q: torch.Tensor, k: torch.Tensor, packed_v: torch.Tensor, *,
                    split_workspace: Optional[torch.Tensor] = None, prepare: bool = False):
     """prefill() with V taken from a workspace filled by prefill_pack_v (same shapes).
     With split_workspace (a zero-filled uint8 GPU tensor of at least
-    prefill_split_workspace_size(...) bytes, reusable across calls), the key
+    prefill_split_workspace_size(...) bytes, reusable across calls of any shape
+    it is large enough for: its arrival counters sit at a fixed place), the key
     ranges of the longest query blocks are split over two work-groups
     (fa_prefill_fwd_packed_split). With prepare=True, returns a callable that
     repeats the call (pass the outputs)."""

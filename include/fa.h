@@ -174,9 +174,15 @@ int fa_prefill_fwd_packed(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_s
  * Same arguments, checks and results as fa_prefill_fwd_packed, plus
  * split_workspace: caller-owned device scratch of at least
  * fa_prefill_split_workspace_size(batch, seqlen_q, n_heads_q, head_dim)
- * bytes, 256-byte aligned, zero-filled before its first use; every call
- * leaves the arrival counters it uses at zero again, so one fill serves
- * any number of later calls. Calls that overlap in time must not share it.
+ * bytes, 256-byte aligned, zero-filled before its first use. Its first 64
+ * KiB hold the arrival counters (one per 128-row query block of every batch
+ * entry and query head) at the same place for every shape, and every call
+ * leaves the counters it uses at zero again, so one fill serves any number
+ * of later calls, of any shapes the buffer is large enough for. The rest
+ * holds partial results, written before they are read within each call.
+ * Shapes with more than 16384 query blocks (batch * n_heads_q *
+ * ceil(seqlen_q / 128)) run unsplit. Calls that overlap in time must not
+ * share the buffer.
  *
  * Under causal masks (and windows) the 128-row query blocks see different
  * numbers of key tiles, and a launch cannot end before its longest block
@@ -205,10 +211,10 @@ int fa_prefill_fwd_packed_split(const void* q, int64_t q_sb, int64_t q_ss, int64
 
 /*
  * fa_prefill_split_workspace_size — bytes of split_workspace
- * fa_prefill_fwd_packed_split needs: for every 128-row query block of every
- * (batch entry, query head), a 4-byte counter and two halves of partial
- * results (128 x head_dim fp32 O and 128 fp32 LSE each), i.e. about
- * 2 * batch * n_heads_q * ceil(seqlen_q / 128) * 128 * (head_dim + 1) * 4.
+ * fa_prefill_fwd_packed_split needs: 64 KiB of arrival counters, then for
+ * every 128-row query block of every (batch entry, query head) two halves of
+ * partial results (128 x head_dim fp32 O and 128 fp32 LSE each), i.e. about
+ * 65536 + 2 * batch * n_heads_q * ceil(seqlen_q / 128) * 128 * (head_dim + 1) * 4.
  * Returns 0 for non-positive sizes. Host only; never fails otherwise.
  */
 uint64_t fa_prefill_split_workspace_size(int batch, int seqlen_q, int n_heads_q, int head_dim);
@@ -236,7 +242,8 @@ uint64_t fa_prefill_split_workspace_size(int batch, int seqlen_q, int n_heads_q,
  * half of its key tiles (floor(n / 2) of n), 2 = the second half. Every block
  * appears either whole or as both halves. Returns -FA_ERR_INVALID_ARG (a
  * negative count) for non-positive sizes, bad head counts, window < 0 or
- * max_units < 0; head dims other than 64 and 128 get 0.
+ * max_units < 0; head dims other than 64 and 128, and shapes with more than
+ * 16384 query blocks (the arrival counters' capacity), get 0.
  */
 int fa_prefill_split_units(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
                            int head_dim, int causal, int window, uint16_t* units, int max_units);

@@ -60,6 +60,7 @@ def _split_runs(torch, q, k, v, dtype, *, causal, scale, window=0, lens=None, si
     sws = torch.zeros(fa.prefill_split_workspace_size(B, Sq, Hq, D), dtype=torch.uint8,
                       device="cuda")
     n_cnt = B * Hq * (-(-Sq // 128))
+    assert n_cnt * 4 <= 65536
     runs = []
     for _ in range(repeats):
         out = torch.full((B, Sq, Hq, D), float("nan"), device="cuda")
@@ -161,3 +162,40 @@ def test_one_call_prefill_with_split_workspace(torch_gpu):
     torch.cuda.synchronize()
     assert o1.cpu().numpy().tobytes() == o2.cpu().numpy().tobytes()
     assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes()
+
+
+def test_split_workspace_reused_across_shapes(torch_gpu):
+    """One split workspace, zero-filled once, serves calls of different shapes
+    and inputs: a small shape, a larger one, then the small one again with new
+    inputs. The counters live in a fixed region at the start of the buffer, so
+    no call's partial results land on another shape's counters; every call is
+    checked against the oracle (none is the first call on a fresh buffer) and
+    all counters are zero after each call."""
+    from flashattention_attention_amd import fa
+    torch = torch_gpu
+    _say("split workspace reused across shapes")
+    shapes = [  # B, S, Hq, Hkv, D, dtype
+        (1, 1000, 8, 8, 64, "f16"),
+        (1, 4096, 8, 4, 128, "bf16"),
+        (1, 1000, 8, 8, 64, "f16"),
+    ]
+    size = max(fa.prefill_split_workspace_size(B, S, Hq, D) for B, S, Hq, _, D, _ in shapes)
+    assert size >= 65536
+    sws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for i, (B, S, Hq, Hkv, D, dtype) in enumerate(shapes):
+        assert fa.prefill_split_units(B, S, S, Hq, Hkv, D, True, 0), "planner must split"
+        rng = np.random.default_rng(100 + i)
+        q = inputs.draw_half(rng, (B, S, Hq, D), dtype)
+        k = inputs.draw_half(rng, (B, S, Hkv, D), dtype)
+        v = inputs.draw_half(rng, (B, S, Hkv, D), dtype)
+        scale = float(np.float32(1 / np.sqrt(D)))
+        o, lse = fa.prefill_packed(_dev(torch, q, dtype), _dev(torch, k, dtype),
+                                   fa.prefill_pack_v(_dev(torch, v, dtype)), causal=True,
+                                   softmax_scale=scale, split_workspace=sws)
+        torch.cuda.synchronize()
+        assert int(sws[:65536].view(torch.int32).abs().sum().item()) == 0, \
+            f"arrival counters not back at zero after call {i}"
+        # every row of the small shape; the last two blocks (split) and samples of the large one
+        rows = None if S <= 1000 else sorted({0, 1, 127, 128, S // 2} | set(range(S - 256, S)))
+        ref = oracle.prefill(q, k, v, scale=scale, causal=True, dtype=dtype, rows=rows)
+        _check(o.cpu().numpy(), lse.cpu().numpy(), ref, rows=rows)

@@ -115,13 +115,23 @@ def test_plan_examples():
 
 
 def test_split_workspace_size():
+    # 64 KiB of arrival counters at offset 0 for every shape, then the partial
+    # LSEs and outputs of the two halves of every query block
     lib = fa.load_library()
     blocks = 1 * 28 * 26
     up = lambda x: (x + 255) // 256 * 256
-    want = up(blocks * 4) + up(blocks * 2 * 128 * 4) + blocks * 2 * 128 * 128 * 4
+    want = 65536 + up(blocks * 2 * 128 * 4) + blocks * 2 * 128 * 128 * 4
     assert lib.fa_prefill_split_workspace_size(1, 3314, 28, 128) == want
     assert lib.fa_prefill_split_workspace_size(0, 3314, 28, 128) == 0
-    assert lib.fa_prefill_split_workspace_size(1, 1, 1, 64) == 256 + 1024 + 2 * 128 * 64 * 4
+    assert lib.fa_prefill_split_workspace_size(1, 1, 1, 64) == 65536 + 1024 + 2 * 128 * 64 * 4
+
+
+def test_split_counter_capacity():
+    # one counter per 128-row query block of every (batch entry, query head):
+    # 16384 fit in the fixed region; a shape with more runs unsplit
+    few = fa.prefill_split_units(1, 8192, 8192, 8, 8, 128, True, 0)
+    assert few, "a long prompt over few heads splits"
+    assert fa.prefill_split_units(1, 16384, 16384, 129, 129, 64, True, 0) == []
 
 
 def _gpu_visible():
