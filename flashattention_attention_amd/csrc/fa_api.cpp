@@ -466,6 +466,25 @@ int fa_decode_split_partial(const void* q, int64_t q_sb, int64_t q_sh,
                     "fa_decode_split_partial launch");
 }
 
+// The single-launch decode on a validated call with its scratch at ws (layout f).
+static int launch_fused(const void* q, int64_t q_sb, int64_t q_sh, const void* k_cache,
+                        const void* v_cache, int64_t kv_stride_tok, int64_t kv_stride_head,
+                        const int64_t* kv_offsets, const int32_t* kv_lens, int batch,
+                        int n_heads_q, int n_heads_kv, int head_dim, int dtype,
+                        float softmax_scale, int split_len, int max_splits, float* o, float* lse,
+                        const fa::FusedLayout& f, char* ws, void* stream, const char* what) {
+  fa::DecodeArgs a = decode_args(q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok, kv_stride_head,
+                                 kv_offsets, kv_lens, batch, n_heads_q, n_heads_kv,
+                                 softmax_scale, split_len, max_splits);
+  a.o = o; a.lse = lse;
+  a.counters = (int*)(ws + f.counters);
+  a.wg_lse = (float*)(ws + f.wg_lse);
+  a.wg_o = (float*)(ws + f.wg_o);
+  a.max_wg = f.max_wg;
+  return hip_status(fa::launch_decode_fused(a, head_dim, dtype == FA_BF16, (hipStream_t)stream),
+                    what);
+}
+
 int fa_decode_fused(const void* q, int64_t q_sb, int64_t q_sh,
                     const void* k_cache, const void* v_cache,
                     int64_t kv_stride_tok, int64_t kv_stride_head,
@@ -488,17 +507,42 @@ int fa_decode_fused(const void* q, int64_t q_sb, int64_t q_sh,
   if (!workspace || workspace_bytes < f.total || ((uintptr_t)workspace & 255u))
     return fail(FA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned and hold %llu bytes",
                 fn, (unsigned long long)f.total);
-  fa::DecodeArgs a = decode_args(q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok, kv_stride_head,
-                                 kv_offsets, kv_lens, batch, n_heads_q, n_heads_kv,
-                                 softmax_scale, split_len, max_splits);
-  char* ws = (char*)workspace;
-  a.o = o; a.lse = lse;
-  a.counters = (int*)(ws + f.counters);
-  a.wg_lse = (float*)(ws + f.wg_lse);
-  a.wg_o = (float*)(ws + f.wg_o);
-  a.max_wg = f.max_wg;
-  return hip_status(fa::launch_decode_fused(a, head_dim, dtype == FA_BF16, (hipStream_t)stream),
-                    "fa_decode_fused launch");
+  return launch_fused(q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok, kv_stride_head, kv_offsets,
+                      kv_lens, batch, n_heads_q, n_heads_kv, head_dim, dtype, softmax_scale,
+                      split_len, max_splits, o, lse, f, (char*)workspace, stream,
+                      "fa_decode_fused launch");
+}
+
+int fa_decode_fused_noalloc(const void* q, int64_t q_sb, int64_t q_sh,
+                            const void* k_cache, const void* v_cache,
+                            int64_t kv_stride_tok, int64_t kv_stride_head,
+                            const int64_t* kv_offsets, const int32_t* kv_lens,
+                            int batch, int n_heads_q, int n_heads_kv, int head_dim, int dtype,
+                            float softmax_scale, int split_len, int max_splits,
+                            float* o, float* lse, void* stream) {
+  const char* fn = "fa_decode_fused_noalloc";
+  if (!o || !lse) return fail(FA_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  const int st = check_decode(fn, q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok,
+                              kv_stride_head, kv_offsets, kv_lens, batch, n_heads_q, n_heads_kv,
+                              head_dim, dtype, softmax_scale, split_len, max_splits);
+  if (st != FA_OK) return st;
+  const fa::FusedLayout f =
+      fa::decode_fused_layout(batch, n_heads_q, n_heads_kv, head_dim, max_splits);
+  if (f.n_counters * (int64_t)sizeof(int) > (int64_t)fa::kFusedCounterBytes)
+    return fail(FA_ERR_UNSUPPORTED, "%s: batch * head groups (%lld) above %d", fn,
+                (long long)f.n_counters, (int)(fa::kFusedCounterBytes / sizeof(int)));
+  if (f.total > fa::kNoAllocScratchBytes)
+    return fail(FA_ERR_UNSUPPORTED,
+                "%s: this shape needs %llu bytes of scratch, above the library's %llu "
+                "(use fa_decode_fused with a caller workspace)", fn,
+                (unsigned long long)f.total, (unsigned long long)fa::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = fa::decode_noalloc_scratch(&ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "fa_decode_fused_noalloc scratch set-up");
+  return launch_fused(q, q_sb, q_sh, k_cache, v_cache, kv_stride_tok, kv_stride_head, kv_offsets,
+                      kv_lens, batch, n_heads_q, n_heads_kv, head_dim, dtype, softmax_scale,
+                      split_len, max_splits, o, lse, f, (char*)ws, stream,
+                      "fa_decode_fused_noalloc launch");
 }
 
 uint64_t fa_decode_fused_workspace_size(int batch, int n_heads_q, int n_heads_kv, int head_dim,

@@ -32,8 +32,23 @@
 // deterministic for a given split plan.
 #include "fa_internal.h"
 
+#include <mutex>
+
+// Scratch of the single-launch decode for callers that cannot allocate
+// (fa_decode_fused_noalloc): one copy per GPU, held until the process ends.
+// In host code this name only stands for the array; its device address is
+// looked up per device (decode_noalloc_scratch) and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[fa::kNoAllocScratchBytes];
+
 namespace fa {
 namespace {
+
+// Zeroes n 32-bit words (the arrival counters of the scratch, once per device).
+__global__ void __launch_bounds__(256) zero_words_kernel(int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -890,6 +905,37 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, bool bf16,
                           : launch_partial_d<256, false>(a, g, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t decode_noalloc_scratch(void** out, hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    // With this device current: the address of this device's copy of the array.
+    void* p = nullptr;
+    hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r == hipSuccess && p == nullptr) r = hipErrorInvalidSymbol;
+    if (r == hipSuccess) {
+      // The array starts zeroed when the code object loads; the counter region
+      // is cleared once more here (a kernel, not a memset, so that a first call
+      // made under stream capture records an ordinary kernel node), and every
+      // call returns its counters to zero.
+      constexpr int n = (int)(kFusedCounterBytes / sizeof(int));
+      hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, (int*)p, n);
+      r = hipGetLastError();
+    }
+    addr[dev] = p;
+    status[dev] = r;
+  });
+  if (status[dev] != hipSuccess) return status[dev];
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {

@@ -126,6 +126,13 @@ hipError_t launch_decode_merge(const MergeArgs& a, int head_dim, hipStream_t str
 hipError_t launch_decode_fused(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_branch_merge(const BranchMergeArgs& a, int head_dim, hipStream_t stream);
 
+// Library-owned scratch of the single-launch decode for callers that cannot
+// allocate (one static array per GPU; see fa_decode_fused_noalloc in fa.h).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+// Device address of the current device's scratch; the first call on a device
+// looks it up and clears its counter region with a kernel on `stream`.
+hipError_t decode_noalloc_scratch(void** out, hipStream_t stream);
+
 // Splits (one per wave) merged inside one work-group of the single-launch decode.
 int decode_fused_waves(int batch, int n_heads_q, int n_heads_kv, int head_dim, int max_splits);
 // Workspace of the single-launch decode, and the offsets of its parts.

@@ -56,6 +56,9 @@ _SIGNATURES = {
     "fa_decode_fused": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
                          _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp,
                          _vp, ctypes.c_uint64, _vp], _i32),
+    "fa_decode_fused_noalloc": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
+                                 _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp,
+                                 _vp], _i32),
     "fa_decode_fused_workspace_size": ([_i32, _i32, _i32, _i32, _i32], ctypes.c_uint64),
     "fa_decode_fused_waves": ([_i32, _i32, _i32, _i32, _i32], _i32),
     "fa_status_string": ([_i32], ctypes.c_char_p),
@@ -525,6 +528,35 @@ def decode_fused(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(dev)),
         (q, k_cache, v_cache, kv_offsets, kv_lens, out, lse, workspace), prepare)
+    return call if prepare else (out, lse)
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_fused_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         kv_offsets: torch.Tensor, kv_lens: torch.Tensor, *, split_len: int,
+                         max_splits: int, softmax_scale: Optional[float] = None,
+                         out: torch.Tensor, lse: torch.Tensor, prepare: bool = False):
+    """decode_fused with the library's own scratch (fa_decode_fused_noalloc):
+    the caller passes the outputs (contiguous fp32 [B,Hq,D] and [B,Hq]) and
+    nothing is allocated. Calls that overlap in time on one GPU must not be
+    issued (they share that GPU's scratch)."""
+    dev = _check_decode_inputs(q, k_cache, v_cache, kv_offsets, kv_lens)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
+    _on_gpu(out, lse)
+    if out.shape != (B, Hq, D) or lse.shape != (B, Hq) or not out.is_contiguous() \
+            or not lse.is_contiguous() or out.dtype != torch.float32 \
+            or lse.dtype != torch.float32:
+        raise FAError("out / lse must be contiguous fp32 [B,Hq,D] / [B,Hq]")
+    call = _issue("fa_decode_fused_noalloc", (
+        q.data_ptr(), q.stride(0), q.stride(1), k_cache.data_ptr(), v_cache.data_ptr(),
+        k_cache.stride(0), k_cache.stride(1), kv_offsets.data_ptr(), kv_lens.data_ptr(),
+        B, Hq, Hkv, D, _dtype_code(q), scale, split_len, max_splits,
+        out.data_ptr(), lse.data_ptr(), _stream(dev)),
+        (q, k_cache, v_cache, kv_offsets, kv_lens, out, lse), prepare)
     return call if prepare else (out, lse)
 
 

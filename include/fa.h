@@ -401,6 +401,33 @@ int fa_decode_fused(const void* q, int64_t q_sb, int64_t q_sh,
                     void* stream);
 
 /*
+ * fa_decode_fused_noalloc — fa_decode_fused without a caller workspace.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments (minus the workspace), checks, kernels and results as
+ * fa_decode_fused: the bytes of o and lse equal those fa_decode_fused
+ * writes for the same call. The scratch (arrival counters and work-group
+ * partials) is a library-owned static device array of
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held until the process
+ * ends; the call allocates and frees nothing. The first call on a device
+ * looks up that device's copy and enqueues one small kernel on `stream` that
+ * clears its 64 KiB of counters; every call leaves them at zero again.
+ * Shapes whose fa_decode_fused_workspace_size exceeds the array return
+ * FA_ERR_UNSUPPORTED (use fa_decode_fused with a caller workspace). All calls
+ * on one GPU share its array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_decode_fused_noalloc(const void* q, int64_t q_sb, int64_t q_sh,
+                            const void* k_cache, const void* v_cache,
+                            int64_t kv_stride_tok, int64_t kv_stride_head,
+                            const int64_t* kv_offsets, const int32_t* kv_lens,
+                            int batch, int n_heads_q, int n_heads_kv, int head_dim, int dtype,
+                            float softmax_scale, int split_len, int max_splits,
+                            float* o, float* lse, void* stream);
+
+/*
  * fa_decode_fused_workspace_size — bytes of workspace fa_decode_fused needs
  * (0 for invalid sizes). fa_decode_fused_waves — splits one work-group of
  * fa_decode_fused merges on chip (0 for invalid sizes). Host only.

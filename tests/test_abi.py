@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"fa_prefill_fwd", "fa_prefill_pack_v", "fa_prefill_fwd_packed",
                           "fa_prefill_workspace_size", "fa_decode_plan",
                           "fa_decode_split_partial", "fa_decode_merge_lse", "fa_decode_fused",
+                          "fa_decode_fused_noalloc",
                           "fa_decode_fused_workspace_size", "fa_decode_fused_waves",
                           "fa_attn_merge", "fa_prefill_fwd_packed_split",
                           "fa_prefill_split_workspace_size", "fa_prefill_split_units",
@@ -202,6 +203,29 @@ def test_decode_fused_validation(kw, status):
     st = lib.fa_decode_fused(b["q"], 512, 128, b["k"], b["v"], 256, 128, b["offs"], b["lens"],
                              b["B"], b["Hq"], b["Hkv"], b["D"], b["dtype"], b["scale"],
                              b["split"], b["ms"], b["o"], b["lse"], b["ws"], b["wsb"], None)
+    assert st == status, lib.fa_last_error()
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="host-validation probes run only without a GPU")
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(lse=None), 1), (dict(q=None), 1), (dict(D=96), 2),
+    (dict(Hkv=3), 1), (dict(split=24), 1),
+    # needs more scratch than the library's 16 MiB array: unsupported, use the workspace form
+    (dict(B=64, Hq=32, Hkv=8, ms=64), 2),
+    # more arrival counters than the fixed 64 KiB region holds
+    (dict(B=20000, Hq=4, Hkv=2, ms=1), 2),
+])
+def test_decode_fused_noalloc_validation(kw, status):
+    # the allocation-free form checks as the workspace form does, plus its
+    # scratch limit, all on the host before any HIP call
+    b = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, offs=ALIGNED, lens=ALIGNED, o=ALIGNED, lse=ALIGNED,
+             B=1, Hq=4, Hkv=2, D=128, dtype=0, scale=0.1, split=32, ms=4)
+    b.update(kw)
+    lib = fa.load_library()
+    assert lib.fa_decode_fused_workspace_size(64, 32, 8, 128, 64) > 16 << 20
+    st = lib.fa_decode_fused_noalloc(b["q"], 512, 128, b["k"], b["v"], 256, 128, b["offs"],
+                                     b["lens"], b["B"], b["Hq"], b["Hkv"], b["D"], b["dtype"],
+                                     b["scale"], b["split"], b["ms"], b["o"], b["lse"], None)
     assert st == status, lib.fa_last_error()
 
 
