@@ -3,9 +3,12 @@
 Gate (from the method's statement of the problem): max |O_gpu - O_ref| <= 2e-3
 and max |LSE_gpu - LSE_ref| <= 1e-4 (natural log), element by element, for
 half-precision inputs with fp32 accumulation; outputs byte-identical run to
-run. Small problems are compared in full; the full-size workloads are compared
-on sampled rows (or sampled heads for decode) that the oracle computes one by
-one, in the same launch configuration the benchmark times.
+run. Small problems are compared in full. At full size, in the launch
+configuration the benchmark times, the GQA prompt (3314 rows x 28 heads) and
+the batched long decode (every sequence and head) are compared in full; the
+large-head prompt, whose full fp64 reference would take minutes, is compared on
+three rows of every 128-row query block (its first, its last and one drawn
+from seed) plus fixed boundary rows, which the oracle computes one by one.
 """
 import numpy as np
 import pytest
@@ -82,7 +85,12 @@ def test_tiny_workload_full(torch_gpu):
 
 SWEEP = []
 for D in (64, 128, 256):
-    for S in (1, 2, 31, 33, 64, 65, 127, 129, 1000):
+    # ragged and whole tiles (32-key tiles at head_dim 256, 64 below), one and
+    # several 128-row query blocks, and the 3314-token prompt length
+    lengths = (1, 2, 31, 33, 64, 65, 127, 129, 1000)
+    if D >= 128:
+        lengths += (32, 63, 128, 3314)
+    for S in lengths:
         hq, hkv = (7, 1) if S % 2 else (8, 2)
         SWEEP.append((1, S, S, hq, hkv, D, "bf16" if S % 3 else "f16", True, False))
 SWEEP += [
@@ -164,14 +172,24 @@ def _sample_rows(S, n_random, seed):
     return sorted(r for r in fixed if 0 <= r < S)
 
 
-def _full_size_prefill(torch, cfg, n_random):
+def _block_rows(S, seed, block=128):
+    """The first and last row of every 128-row query block, one row drawn from
+    seed inside each block, and the fixed boundary rows."""
+    rng = np.random.default_rng(seed)
+    rows = set(_sample_rows(S, 0, seed))
+    for b0 in range(0, S, block):
+        b1 = min(S, b0 + block) - 1
+        rows |= {b0, b1, int(rng.integers(b0, b1 + 1))}
+    return sorted(rows)
+
+
+def _full_size_prefill(torch, cfg, rows):
     from flashattention_attention_amd import fa
     x = inputs.make_prefill_inputs(cfg)
     runs = [_run_prefill(torch, fa, x["q"], x["k"], x["v"], cfg.dtype, cfg.causal, cfg.scale,
                          unnorm=cfg.out_unnormalized) for _ in range(2)]
     for a, b in zip(runs[0], runs[1]):                     # determinism: identical bytes
         assert a.tobytes() == b.tobytes()
-    rows = _sample_rows(cfg.seqlen_q, n_random, cfg.seed)
     ref = oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=cfg.causal,
                          dtype=cfg.dtype, rows=rows)
     o, lse, rs = runs[0]
@@ -180,13 +198,22 @@ def _full_size_prefill(torch, cfg, n_random):
 
 
 def test_gqa_prefill_full_size(torch_gpu):
+    """Every element of O and LSE (3314 rows x 28 heads) against the oracle;
+    the fp64 reference of the whole prompt takes ~5 s on 8 host cores."""
     _say(inputs.GQA_PREFILL.name)
-    _full_size_prefill(torch_gpu, inputs.GQA_PREFILL, 24)
+    _full_size_prefill(torch_gpu, inputs.GQA_PREFILL, None)
 
 
 def test_large_head_prefill_full_size(torch_gpu):
-    _say(inputs.LARGE_HEAD.name)
-    _full_size_prefill(torch_gpu, inputs.LARGE_HEAD, 8)
+    """Three rows of each of the 64 query blocks (first, last, one drawn from
+    seed) plus the boundary rows, every head of both batch entries (~200 rows x
+    32 heads, ~2 s of oracle time on 8 host cores); the un-normalized output
+    is normalized in fp64 and row_sum gated in log space."""
+    cfg = inputs.LARGE_HEAD
+    _say(cfg.name)
+    rows = _block_rows(cfg.seqlen_q, cfg.seed)
+    assert len(rows) >= 3 * (cfg.seqlen_q // 128)
+    _full_size_prefill(torch_gpu, cfg, rows)
 
 
 # ---------------------------------------------------------------------------
@@ -300,15 +327,10 @@ def test_long_decode_full_size(torch_gpu):
     assert outs[0][0].tobytes() == outs[1][0].tobytes()
     assert outs[0][1].tobytes() == outs[1][1].tobytes()
     o, lse = outs[0]
-    rng = np.random.default_rng(4)
-    picks = {(int(np.argmax(x["kv_lens"])), 0), (int(np.argmin(x["kv_lens"])), cfg.n_heads_q - 1)}
-    picks |= {(int(b), int(h)) for b, h in zip(rng.integers(0, cfg.batch, 14),
-                                                rng.integers(0, cfg.n_heads_q, 14))}
-    for b, h in sorted(picks):
-        sub = {"q": x["q"][b:b + 1, h:h + 1], "kv_lens": x["kv_lens"][b:b + 1],
-               "kv_offsets": x["kv_offsets"][b:b + 1]}
-        hk = h // (cfg.n_heads_q // cfg.n_heads_kv)
-        ref = oracle.decode(sub["q"], x["k_cache"][:, hk:hk + 1], x["v_cache"][:, hk:hk + 1],
-                            sub["kv_offsets"], sub["kv_lens"], scale=cfg.scale, dtype=cfg.dtype)
-        assert np.abs(o[b, h] - ref["o"][0, 0]).max() <= O_TOL, (b, h)
-        assert abs(lse[b, h] - ref["lse"][0, 0]) <= LSE_TOL, (b, h)
+    # every (sequence, query head): ~18 s of oracle time on 8 host cores
+    ref = oracle.decode(x["q"], x["k_cache"], x["v_cache"], x["kv_offsets"], x["kv_lens"],
+                        scale=cfg.scale, dtype=cfg.dtype)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    err_o = np.abs(o - ref["o"]).max()
+    err_l = np.abs(lse - ref["lse"]).max()
+    assert err_o <= O_TOL and err_l <= LSE_TOL, f"O err {err_o:.3e}, LSE err {err_l:.3e}"
