@@ -177,11 +177,23 @@ def measured_traffic(kernel, workload, source):
     return None
 
 
+_DECODE_INPUTS = {}
+
+
+def decode_inputs(cfg):
+    """Seeded decode inputs, drawn once per workload (the batched long decode's
+    1.3 G half values take tens of seconds to draw)."""
+    from flashattention_attention_amd import inputs
+    if cfg.name not in _DECODE_INPUTS:
+        _DECODE_INPUTS[cfg.name] = inputs.make_decode_inputs(cfg)
+    return _DECODE_INPUTS[cfg.name]
+
+
 def decode_setup(torch, fa, cfg, split_len=None, head_major=False):
     """head_major: the same caches stored [Hkv, T, D] (passed as [T, Hkv, D] views
     with a head stride of T*D); the default is token-major [T, Hkv, D]."""
     from flashattention_attention_amd import inputs
-    x = inputs.make_decode_inputs(cfg)
+    x = decode_inputs(cfg)
     q, kc, vc = (_dev(torch, x[n], cfg.dtype) for n in ("q", "k_cache", "v_cache"))
     if head_major:
         kc, vc = (t.permute(1, 0, 2).contiguous().permute(1, 0, 2) for t in (kc, vc))
@@ -233,39 +245,75 @@ def time_calls(torch, fns, iters, flush=None):
         torch.cuda.synchronize()
         for i in range(len(fns)):
             per[i].append(evs[i].elapsed_time(evs[i + 1]))
-    return [{"median_ms": statistics.median(p), "min_ms": min(p), "mean_ms": statistics.mean(p)}
-            for p in per]
+    return [_stats(p) for p in per]
+
+
+def _stats(p):
+    """Median, min and mean of interval times (ms), the min/median spread, and
+    how many intervals exceed 1.5x the median (a host stall inside an event
+    interval shows as such an outlier; the median is what the lines report)."""
+    med = statistics.median(p)
+    return {"median_ms": med, "min_ms": min(p), "mean_ms": statistics.mean(p),
+            "spread": round((med - min(p)) / med, 4) if med > 0 else 0.0,
+            "outliers": sum(1 for x in p if x > 1.5 * med)}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _nproc():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _prefill_pairs(cfg, rows):
+    """Visible (query, key) pairs of the listed rows (causal, bottom-right)."""
+    off = cfg.seqlen_kv - cfg.seqlen_q
+    if not cfg.causal:
+        return len(rows) * cfg.seqlen_kv
+    return int(sum(min(cfg.seqlen_kv, r + off + 1) for r in rows))
+
+
+def _oracle_prefill_rate(cfg, x, rows):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=cfg.causal, dtype=cfg.dtype,
+                   rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4 * cfg.head_dim * cfg.n_heads_q * cfg.batch * _prefill_pairs(cfg, rows)
+    return flops, dt
 
 
 def cpu_baseline(budget_s=20.0):
-    """fp64 oracle on a bounded sample of the prefill workload (rows spread over
-    the sequence, all heads), doubling the sample until ~budget_s of CPU work."""
+    """The fp64 oracle timed on this host. The contract figure: a bounded sample
+    of the GQA prompt (rows spread over the sequence, all heads), doubled until
+    ~budget_s / 2 of CPU work (the whole prompt takes ~2 s on 16 threads), and
+    the same oracle on one thread. per_config: the oracle on every workload,
+    whole or on a stated sample, in the unit of the GPU figure."""
     import oracle
     from flashattention_attention_amd import inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     cfg = inputs.GQA_PREFILL
     x = inputs.make_prefill_inputs(cfg)
     n, spent, last = 16, 0.0, None
     while True:
         rows = np.unique(np.linspace(0, cfg.seqlen_q - 1, n).astype(np.int64))
-        t0 = time.perf_counter()
-        oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=cfg.causal,
-                       dtype=cfg.dtype, rows=rows)
-        dt = time.perf_counter() - t0
+        flops, dt = _oracle_prefill_rate(cfg, x, rows)
         spent += dt
-        off = cfg.seqlen_kv - cfg.seqlen_q
-        flops = 4 * cfg.head_dim * cfg.n_heads_q * cfg.batch * int(sum(r + off + 1 for r in rows))
         last = (len(rows), dt, flops)
         if spent >= budget_s / 2 or n >= cfg.seqlen_q:
             break
         n *= 2
     nrows, dt, flops = last
     out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-           "kind": "oracle",
+           "nproc": _nproc(), "kind": "oracle",
            "sample": f"{nrows} query rows evenly spaced over the 3314-token prompt, all "
                      f"{cfg.n_heads_q} heads, fp64 two-pass definition ({flops / 1e9:.2f} "
                      f"GFLOP in {dt:.2f} s)"}
@@ -273,17 +321,64 @@ def cpu_baseline(budget_s=20.0):
         from threadpoolctl import threadpool_limits
         rows = np.unique(np.linspace(0, cfg.seqlen_q - 1, 128).astype(np.int64))
         with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=cfg.causal,
-                           dtype=cfg.dtype, rows=rows)
-            dt1 = time.perf_counter() - t0
-        off = cfg.seqlen_kv - cfg.seqlen_q
-        f1 = 4 * cfg.head_dim * cfg.n_heads_q * cfg.batch * int(sum(r + off + 1 for r in rows))
+            f1, dt1 = _oracle_prefill_rate(cfg, x, rows)
         out["single_thread"] = {"value": f1 / dt1 / 1e12, "unit": "TFLOP/s",
                                 "sample": f"{len(rows)} query rows, all heads "
                                           f"({f1 / 1e9:.2f} GFLOP in {dt1:.2f} s)"}
     except ImportError:
         pass
+
+    per = {cfg.name: {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s",
+                      "seconds": round(dt, 3), "sample": f"{nrows} of {cfg.seqlen_q} rows"}}
+    # the tiny prompt, whole
+    tcfg = inputs.TINY_CAUSAL
+    tx = inputs.make_prefill_inputs(tcfg)
+    rows = np.arange(tcfg.seqlen_q)
+    f, d = _oracle_prefill_rate(tcfg, tx, rows)
+    per[tcfg.name] = {"value": round(f / d / 1e12, 6), "unit": "TFLOP/s",
+                      "us_per_call": round(d * 1e6, 1), "seconds": round(d, 4),
+                      "sample": "whole problem"}
+    # the large-head prompt: 32 rows evenly spaced, every head of both batch entries
+    hcfg = inputs.LARGE_HEAD
+    hx = inputs.make_prefill_inputs(hcfg)
+    rows = np.unique(np.linspace(0, hcfg.seqlen_q - 1, 32).astype(np.int64))
+    f, d = _oracle_prefill_rate(hcfg, hx, rows)
+    per[hcfg.name] = {"value": round(f / d / 1e12, 5), "unit": "TFLOP/s", "seconds": round(d, 3),
+                      "sample": f"{len(rows)} of {hcfg.seqlen_q} rows, all 32 (batch, head)"}
+    del hx
+    # decode: the 1641-token call whole; the batched long decode on a sample of
+    # (sequence, head) pairs, its whole-call time scaled by the keys visited
+    for dcfg, n_pairs in ((inputs.GQA_DECODE, None), (inputs.LONG_DECODE, 16)):
+        dx = decode_inputs(dcfg)
+        kv_bytes = inputs.decode_kv_bytes(dx["kv_lens"], dcfg.n_heads_kv, dcfg.head_dim)
+        if n_pairs is None:
+            t0 = time.perf_counter()
+            oracle.decode(dx["q"], dx["k_cache"], dx["v_cache"], dx["kv_offsets"],
+                          dx["kv_lens"], scale=dcfg.scale, dtype=dcfg.dtype)
+            call_s = time.perf_counter() - t0
+            sample = "whole call"
+        else:
+            rng = np.random.default_rng(dcfg.seed)
+            picks = sorted({(int(b), int(h)) for b, h in
+                            zip(rng.integers(0, dcfg.batch, n_pairs),
+                                rng.integers(0, dcfg.n_heads_q, n_pairs))})
+            group = dcfg.n_heads_q // dcfg.n_heads_kv
+            t0 = time.perf_counter()
+            for b, h in picks:
+                hk = h // group
+                oracle.decode(dx["q"][b:b + 1, h:h + 1], dx["k_cache"][:, hk:hk + 1],
+                              dx["v_cache"][:, hk:hk + 1], dx["kv_offsets"][b:b + 1],
+                              dx["kv_lens"][b:b + 1], scale=dcfg.scale, dtype=dcfg.dtype)
+            dt_s = time.perf_counter() - t0
+            keys_sample = sum(int(dx["kv_lens"][b]) for b, _ in picks)
+            keys_all = int(dx["kv_lens"].sum()) * dcfg.n_heads_q
+            call_s = dt_s * keys_all / keys_sample
+            sample = (f"{len(picks)} (sequence, head) pairs in {dt_s:.2f} s, the whole call "
+                      f"scaled by the keys visited")
+        per[dcfg.name] = {"us_per_call": round(call_s * 1e6, 1),
+                          "value": round(kv_bytes / call_s / 1e9, 3), "unit": "GB/s",
+                          "sample": sample}
+    out["per_config"] = per
     return out
 
 
@@ -338,7 +433,7 @@ def run_profiling_aid(torch, fa, inputs, args):
             f()
     torch.cuda.synchronize()
     r = time_calls(torch, fns, args.steps)
-    print(f"[profiling aid] {label}: " + ", ".join(f"{x['mean_ms'] * 1e3:.2f} us" for x in r),
+    print(f"[profiling aid] {label}: " + ", ".join(f"{x['median_ms'] * 1e3:.2f} us" for x in r),
           flush=True)
 
 
@@ -411,10 +506,12 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = statistics.mean(e[0].elapsed_time(e[4]) for e in evs)
 
-    def mean_ms(a, b):
-        return statistics.mean(e[a].elapsed_time(e[b]) for e in evs)
-    pack_mean, attn_mean = mean_ms(0, 1), mean_ms(1, 2)
-    part_mean, merge_mean = mean_ms(2, 3), mean_ms(3, 4)
+    def launch_stats(a, b):
+        return _stats([e[a].elapsed_time(e[b]) for e in evs])
+    st_pack, st_attn, st_part, st_merge = (launch_stats(i, i + 1) for i in range(4))
+    # per-launch medians over the K steps (robust to a host stall in one interval)
+    pack_mean, attn_mean = st_pack["median_ms"], st_attn["median_ms"]
+    part_mean, merge_mean = st_part["median_ms"], st_merge["median_ms"]
     pre_mean = pack_mean + attn_mean
     flops = pcfg.flops()
     value = flops / (pre_mean * 1e-3) / 1e12
@@ -440,12 +537,16 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "wall_ms_per_step": round(wall / K * 1e3, 4),
         "timing": "HIP events between consecutive launches of K eager steps on the launch "
-                  "stream (prepared calls keep the host ahead of the GPU)",
+                  "stream (prepared calls keep the host ahead of the GPU); per-launch figures "
+                  "are medians over the K steps, ms_per_step the mean step interval",
         "config": {"workload": f"{pcfg.name} + {dcfg.name}", "global_batch": 1,
                    "seq_len": pcfg.seqlen_q, "kv_len_decode": 1641, "parallelism": "none"},
         "prefill": {"us_per_call": round(pre_mean * 1e3, 2), "gflop": round(flops / 1e9, 3),
                     "v_repack_us": round(pack_mean * 1e3, 2),
                     "attention_us": round(attn_mean * 1e3, 2),
+                    "attention_us_min": round(st_attn["min_ms"] * 1e3, 2),
+                    "attention_spread": st_attn["spread"],
+                    "attention_outliers": st_attn["outliers"],
                     "frac_mfma_peak": round(value / MI355X_BF16_DENSE_TFLOPS, 4)},
         "decode_gqa_kv1641": {
             "split_len": dinfo["split_len"], "max_splits": dinfo["max_splits"],
@@ -465,7 +566,7 @@ def main():
         # single-token decode: cold (flushed) and hot
         cold = time_calls(torch, [d_partial, d_merge], 20, flush=flush)
         hot = time_calls(torch, [d_partial, d_merge], 50)
-        hot_ms = hot[0]["mean_ms"] + hot[1]["mean_ms"]
+        hot_ms = hot[0]["median_ms"] + hot[1]["median_ms"]
         line["decode_gqa_kv1641"]["cold_us"] = round(
             (cold[0]["median_ms"] + cold[1]["median_ms"]) * 1e3, 2)
         line["decode_gqa_kv1641"]["hot_us"] = round(hot_ms * 1e3, 2)
@@ -473,7 +574,7 @@ def main():
         fh = time_calls(torch, [dinfo["fused"]], 50)
         line["decode_gqa_kv1641"]["fused_single_launch"] = {
             "cold_us": round(fc[0]["median_ms"] * 1e3, 2),
-            "hot_us": round(fh[0]["mean_ms"] * 1e3, 2)}
+            "hot_us": round(fh[0]["median_ms"] * 1e3, 2)}
         if args.split_sweep:
             sweep = {}
             for sl in (16, 32, 48, 64, 112, 208):
@@ -583,14 +684,15 @@ def main():
         hcfg = inputs.LARGE_HEAD
         h_run, h_pack, h_attn = prefill_setup(torch, fa, hcfg)
         h_run()
-        r = time_calls(torch, [h_pack, h_attn], 5)
+        r = time_calls(torch, [h_pack, h_attn], 9)
         hf = hcfg.flops()
-        h_ms = r[0]["mean_ms"] + r[1]["mean_ms"]
+        h_ms = r[0]["median_ms"] + r[1]["median_ms"]
         ht = hf / (h_ms * 1e-3) / 1e12
-        ha = hf / (r[1]["mean_ms"] * 1e-3) / 1e12
+        ha = hf / (r[1]["median_ms"] * 1e-3) / 1e12
         line["prefill_large_head"] = {"workload": hcfg.name,
                                       "us_per_call": round(h_ms * 1e3, 1),
-                                      "attention_us": round(r[1]["mean_ms"] * 1e3, 1),
+                                      "attention_us": round(r[1]["median_ms"] * 1e3, 1),
+                                      "attention_spread": r[1]["spread"],
                                       "tflops": round(ht, 2),
                                       "frac_mfma_peak": round(ht / MI355X_BF16_DENSE_TFLOPS, 4)}
         hk = prefill_kernel_name(hcfg)
@@ -598,7 +700,7 @@ def main():
             "bound": "mfma", "achieved": round(ha, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ha / MI355X_BF16_DENSE_TFLOPS, 4),
             "traffic": measured_traffic(hk, hcfg.name, "fa_prefill.hip"), "kernel": hk,
-            "us_per_launch": round(r[1]["mean_ms"] * 1e3, 1),
+            "us_per_launch": round(r[1]["median_ms"] * 1e3, 1),
             "per_launch": f"{hf / 1e12:.4f} TFLOP"}
         del h_run, h_pack, h_attn
         print("[bench] windowed prefill", file=sys.stderr, flush=True)
@@ -608,11 +710,12 @@ def main():
         w_run()
         r = time_calls(torch, [w_pack, w_attn], 20)
         wf = wcfg.flops()
-        w_ms = r[0]["mean_ms"] + r[1]["mean_ms"]
-        wa = wf / (r[1]["mean_ms"] * 1e-3) / 1e12
+        w_ms = r[0]["median_ms"] + r[1]["median_ms"]
+        wa = wf / (r[1]["median_ms"] * 1e-3) / 1e12
         line["prefill_window"] = {"workload": wcfg.name, "window": wcfg.window,
                                   "us_per_call": round(w_ms * 1e3, 1),
-                                  "attention_us": round(r[1]["mean_ms"] * 1e3, 1),
+                                  "attention_us": round(r[1]["median_ms"] * 1e3, 1),
+                                  "attention_spread": r[1]["spread"],
                                   "tflops": round(wf / (w_ms * 1e-3) / 1e12, 2),
                                   "frac_mfma_peak": round(wf / (w_ms * 1e-3) / 1e12
                                                           / MI355X_BF16_DENSE_TFLOPS, 4)}
@@ -621,7 +724,7 @@ def main():
             "bound": "mfma", "achieved": round(wa, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s", "frac": round(wa / MI355X_BF16_DENSE_TFLOPS, 4),
             "traffic": measured_traffic(wk, wcfg.name, "fa_prefill.hip"), "kernel": wk,
-            "us_per_launch": round(r[1]["mean_ms"] * 1e3, 1),
+            "us_per_launch": round(r[1]["median_ms"] * 1e3, 1),
             "per_launch": f"{wf / 1e12:.4f} TFLOP (visible pairs only)"}
         del w_run, w_pack, w_attn
         print("[bench] windowed prefill with sinks", file=sys.stderr, flush=True)
@@ -638,16 +741,16 @@ def main():
         s_pack(); s_attn(); p_pack2(); p_attn2(); s_merge()
         rf = time_calls(torch, [s_pack, s_attn], 20)
         ru = time_calls(torch, [p_pack2, p_attn2, s_merge], 20)
-        fused_ms = rf[0]["mean_ms"] + rf[1]["mean_ms"]
-        unf_ms = ru[0]["mean_ms"] + ru[1]["mean_ms"] + ru[2]["mean_ms"]
+        fused_ms = rf[0]["median_ms"] + rf[1]["median_ms"]
+        unf_ms = ru[0]["median_ms"] + ru[1]["median_ms"] + ru[2]["median_ms"]
         o_t, l_t = tens["o"], tens["lse"]
         merge_bytes = 2 * (o_t.numel() + l_t.numel()) * 4 + sinks.numel() * 4
-        merge_gbps = merge_bytes / (ru[2]["mean_ms"] * 1e-3) / 1e9
+        merge_gbps = merge_bytes / (ru[2]["median_ms"] * 1e-3) / 1e9
         line["prefill_window_sink"] = {
             "workload": wcfg.name + "_sink", "sinks": "linspace(-2, 6) over the 28 heads",
             "fused_epilogue_us": round(fused_ms * 1e3, 1),
             "unfused_us": round(unf_ms * 1e3, 1),
-            "merge_pass_us": round(ru[2]["mean_ms"] * 1e3, 1),
+            "merge_pass_us": round(ru[2]["median_ms"] * 1e3, 1),
             "fused_tflops": round(wf / (fused_ms * 1e-3) / 1e12, 2)}
         rooflines["attn_merge_sink"] = {
             "bound": "hbm", "achieved": round(merge_gbps, 1), "peak": MI355X_HBM_GBPS,
@@ -655,7 +758,7 @@ def main():
             "traffic": measured_traffic("branch_merge_kernel<128>", wcfg.name + "_sink",
                                         "fa_merge.hip"),
             "kernel": "branch_merge_kernel<128>",
-            "us_per_launch": round(ru[2]["mean_ms"] * 1e3, 1),
+            "us_per_launch": round(ru[2]["median_ms"] * 1e3, 1),
             "per_launch": f"{merge_bytes / 1e6:.2f} MB (O and LSE read and written once)"}
         del s_pack, s_attn, p_pack2, p_attn2, s_merge, tens
         print("[bench] few-heads prefill, unsplit and with the key split", file=sys.stderr,
@@ -672,21 +775,21 @@ def main():
         ru = time_calls(torch, [fu_pack, fu_attn], 20)
         rs = time_calls(torch, [fs_pack, fs_attn], 20)
         ff = fcfg.flops()
-        fu_tf = ff / (ru[1]["mean_ms"] * 1e-3) / 1e12
-        fs_tf = ff / (rs[1]["mean_ms"] * 1e-3) / 1e12
+        fu_tf = ff / (ru[1]["median_ms"] * 1e-3) / 1e12
+        fs_tf = ff / (rs[1]["median_ms"] * 1e-3) / 1e12
         line["prefill_few_heads"] = {
             "workload": fcfg.name, "split_blocks": sum(1 for _, k in units if k == 1),
             "blocks": -(-fcfg.seqlen_q // 128),
-            "attention_us_unsplit": round(ru[1]["mean_ms"] * 1e3, 1),
-            "attention_us_split": round(rs[1]["mean_ms"] * 1e3, 1),
+            "attention_us_unsplit": round(ru[1]["median_ms"] * 1e3, 1),
+            "attention_us_split": round(rs[1]["median_ms"] * 1e3, 1),
             "tflops_unsplit": round(fu_tf, 2), "tflops_split": round(fs_tf, 2),
-            "v_repack_us": round(rs[0]["mean_ms"] * 1e3, 1)}
+            "v_repack_us": round(rs[0]["median_ms"] * 1e3, 1)}
         fk = prefill_kernel_name(fcfg, split=True)
         rooflines["prefill_few_heads_split"] = {
             "bound": "mfma", "achieved": round(fs_tf, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s", "frac": round(fs_tf / MI355X_BF16_DENSE_TFLOPS, 4),
             "traffic": measured_traffic(fk, fcfg.name, "fa_prefill.hip"), "kernel": fk,
-            "us_per_launch": round(rs[1]["mean_ms"] * 1e3, 1),
+            "us_per_launch": round(rs[1]["median_ms"] * 1e3, 1),
             "per_launch": f"{ff / 1e12:.4f} TFLOP"}
         del fu_pack, fu_attn, fs_pack, fs_attn
         print("[bench] head_dim 512 prefill", file=sys.stderr, flush=True)
@@ -694,12 +797,13 @@ def main():
         xcfg = inputs.HD512_PREFILL
         x_run, x_pack, x_attn = prefill_setup(torch, fa, xcfg)
         x_run()
-        r = time_calls(torch, [x_pack, x_attn], 10)
+        r = time_calls(torch, [x_pack, x_attn], 20)
         xf = xcfg.flops()
-        x_ms = r[0]["mean_ms"] + r[1]["mean_ms"]
-        xa = xf / (r[1]["mean_ms"] * 1e-3) / 1e12
+        x_ms = r[0]["median_ms"] + r[1]["median_ms"]
+        xa = xf / (r[1]["median_ms"] * 1e-3) / 1e12
         line["prefill_hd512"] = {"workload": xcfg.name, "us_per_call": round(x_ms * 1e3, 1),
-                                 "attention_us": round(r[1]["mean_ms"] * 1e3, 1),
+                                 "attention_us": round(r[1]["median_ms"] * 1e3, 1),
+                                 "attention_spread": r[1]["spread"],
                                  "tflops": round(xf / (x_ms * 1e-3) / 1e12, 2),
                                  "frac_mfma_peak": round(xf / (x_ms * 1e-3) / 1e12
                                                          / MI355X_BF16_DENSE_TFLOPS, 4)}
@@ -708,7 +812,7 @@ def main():
             "bound": "mfma", "achieved": round(xa, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s", "frac": round(xa / MI355X_BF16_DENSE_TFLOPS, 4),
             "traffic": measured_traffic(xk, xcfg.name, "fa_prefill.hip"), "kernel": xk,
-            "us_per_launch": round(r[1]["mean_ms"] * 1e3, 1),
+            "us_per_launch": round(r[1]["median_ms"] * 1e3, 1),
             "per_launch": f"{xf / 1e12:.4f} TFLOP"}
         del x_run, x_pack, x_attn
         del flush_buf
