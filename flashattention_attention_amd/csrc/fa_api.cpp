@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "fa_internal.h"
 
 namespace {
@@ -74,7 +76,10 @@ int check_attn(const char* fn, const void* q, int64_t q_sb, int64_t q_ss, int64_
   if (o_sb < 0 || o_ss < 0 || o_sh < 0 || o_sb % 4 || o_ss % 4 || o_sh % 4)
     return fail(FA_ERR_INVALID_ARG, "%s: o strides must be non-negative multiples of 4 elements",
                 fn);
-  if ((int64_t)batch * n_heads_q * ((seqlen_q + 127) / 128) > (1 << 30))
+  if (seqlen_kv > (1 << 30) || batch > 65535 || n_heads_kv > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "%s: seqlen_kv above 2^30 or batch / KV heads above 65535",
+                fn);
+  if ((int64_t)batch * n_heads_q * (((int64_t)seqlen_q + 127) / 128) > (1 << 30))
     return fail(FA_ERR_UNSUPPORTED, "%s: grid too large (seqlen_q, heads or batch)", fn);
   if (k_ss > (int64_t)(1 << 23))
     return fail(FA_ERR_UNSUPPORTED, "%s: k sequence stride above 2^23 elements", fn);
@@ -193,6 +198,8 @@ int fa_prefill_pack_v(const void* v, int64_t v_sb, int64_t v_ss, int64_t v_sh, i
     return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256, 512}", fn, head_dim);
   if (dtype != FA_F16 && dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F16 or FA_BF16", fn, dtype);
+  if (seqlen_kv > (1 << 30) || batch > 65535 || n_heads_kv > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "%s: seqlen_kv above 2^30 or batch / heads above 65535", fn);
   int st = check_pack(fn, v, v_sb, v_ss, v_sh);
   if (st == FA_OK)
     st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
@@ -278,7 +285,8 @@ int fa_prefill_fwd_packed_split(const void* q, int64_t q_sb, int64_t q_ss, int64
 }
 
 uint64_t fa_prefill_split_workspace_size(int batch, int seqlen_q, int n_heads_q, int head_dim) {
-  return fa::prefill_split_layout(batch, seqlen_q, n_heads_q, head_dim).total;
+  const size_t t = fa::prefill_split_layout(batch, seqlen_q, n_heads_q, head_dim).total;
+  return t == SIZE_MAX ? 0 : t;
 }
 
 int fa_prefill_split_units(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
@@ -317,7 +325,9 @@ int fa_attn_merge(const float* o_a, int64_t oa_sb, int64_t oa_ss, int64_t oa_sh,
   for (int i = 0; i < 9; ++i)
     if ((i < 3 || i >= 6 || o_b) && (st[i] < 0 || st[i] % 4))
       return fail(FA_ERR_INVALID_ARG, "%s: o strides must be non-negative multiples of 4", fn);
-  if ((int64_t)batch * seqlen * n_heads * (head_dim / 4) > ((int64_t)1 << 40))
+  // one work-item per 16 bytes of O: at most 2^31 of them in the 1-D grid
+  if (fa::sat_mul(fa::sat_mul((size_t)batch, (size_t)seqlen),
+                  fa::sat_mul((size_t)n_heads, (size_t)(head_dim / 4))) > ((size_t)1 << 31))
     return fail(FA_ERR_UNSUPPORTED, "%s: too many rows", fn);
   fa::BranchMergeArgs a;
   a.o_a = o_a; a.lse_a = lse_a; a.o_b = o_b; a.lse_b = lse_b; a.sink_logits = sink_logits;
@@ -332,8 +342,12 @@ int fa_attn_merge(const float* o_a, int64_t oa_sb, int64_t oa_ss, int64_t oa_sh,
 
 uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int head_dim) {
   if (batch < 1 || seqlen_kv < 1 || n_heads_kv < 1 || head_dim < 1) return 0;
-  return fa::prefill_workspace_bytes(batch, seqlen_kv, n_heads_kv, head_dim);
+  const size_t t = fa::prefill_workspace_bytes(batch, seqlen_kv, n_heads_kv, head_dim);
+  return t == SIZE_MAX ? 0 : t;
 }
+
+// Longest KV length the decode planner accepts (2^30 tokens).
+constexpr int kMaxPlanKvLen = 1 << 30;
 
 int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_heads_kv,
                    int head_dim, int num_cus, int* split_len_out, int* max_splits_out) {
@@ -349,10 +363,15 @@ int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_
   for (int b = 0; b < batch; ++b) {
     if (kv_lens_host[b] < 1)
       return fail(FA_ERR_INVALID_ARG, "fa_decode_plan: kv_lens[%d] = %d < 1", b, kv_lens_host[b]);
+    if (kv_lens_host[b] > kMaxPlanKvLen)
+      return fail(FA_ERR_UNSUPPORTED, "fa_decode_plan: kv_lens[%d] = %d above %d", b,
+                  kv_lens_host[b], kMaxPlanKvLen);
     if (kv_lens_host[b] > max_len) max_len = kv_lens_host[b];
   }
   const int g = fa::decode_max_heads_per_wave(n_heads_q / n_heads_kv);
-  const int bk = fa::decode_block_rows(head_dim, g);
+  // split lengths step in whole row blocks of the partial kernel, and in at
+  // least 16 keys (the granularity every decode entry point accepts)
+  const int bk = std::max(16, fa::decode_block_rows(head_dim, g));
   const int64_t slots = (int64_t)num_cus * fa::decode_waves_per_cu(head_dim);
   const int64_t groups = n_heads_q / g;    // waves per (sequence, split)
   auto waves_of = [&](int64_t sl, int64_t* max_ns) {
@@ -375,7 +394,12 @@ int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_
   int best = bk;
   double best_score = -1e300;
   const bool latency_bound = waves_of(bk, nullptr) <= slots;
-  for (int64_t sl = bk;; sl += bk) {
+  // Every whole number of blocks up to the longest sequence is a candidate;
+  // past ~4096 candidates (lengths above 4096 blocks) they are thinned to
+  // multiples of a coarser step, which keeps the plan cheap to compute.
+  const int64_t n_cand = ((int64_t)max_len + bk - 1) / bk;
+  const int64_t step = (int64_t)bk * ((n_cand + 4095) / 4096);
+  for (int64_t sl = bk;; sl += step) {
     int64_t max_ns = 0;
     const int64_t waves = waves_of(sl, &max_ns);
     const int64_t rounds = (waves + slots - 1) / slots;
@@ -389,7 +413,7 @@ int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_
     if (sl >= max_len) break;
   }
   *split_len_out = best;
-  *max_splits_out = (max_len + best - 1) / best;
+  *max_splits_out = (int)(((int64_t)max_len + best - 1) / best);
   return ok();
 }
 
@@ -423,6 +447,9 @@ int check_decode(const char* fn, const void* q, int64_t q_sb, int64_t q_sh, cons
     return fail(FA_ERR_INVALID_ARG, "%s: strides must be non-negative multiples of 8", fn);
   if (max_splits > 2147483647 / 2 || batch > 65535 || n_heads_q > 65535)
     return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  // key positions s * split_len + row of the last split are 32-bit on the device
+  if ((int64_t)split_len * max_splits > 2147483647 - 65536)
+    return fail(FA_ERR_UNSUPPORTED, "%s: split_len * max_splits above the 32-bit key range", fn);
   return FA_OK;
 }
 
@@ -550,7 +577,8 @@ uint64_t fa_decode_fused_workspace_size(int batch, int n_heads_q, int n_heads_kv
   if (batch < 1 || n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0 ||
       !head_dim_supported(head_dim) || max_splits < 1)
     return 0;
-  return fa::decode_fused_layout(batch, n_heads_q, n_heads_kv, head_dim, max_splits).total;
+  const size_t t = fa::decode_fused_layout(batch, n_heads_q, n_heads_kv, head_dim, max_splits).total;
+  return t == SIZE_MAX ? 0 : t;
 }
 
 int fa_decode_fused_waves(int batch, int n_heads_q, int n_heads_kv, int head_dim,

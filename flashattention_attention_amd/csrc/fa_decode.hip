@@ -824,8 +824,9 @@ int decode_fused_waves(int batch, int n_heads_q, int n_heads_kv, int head_dim, i
   if (max_splits <= 16) return 1;
   const int g = decode_heads_per_wave(n_heads_q / n_heads_kv, batch, n_heads_q, head_dim,
                                       max_splits);
-  const int64_t slots = (int64_t)kDecodeCus * decode_waves_per_cu(head_dim);
-  return (int64_t)batch * (n_heads_q / g) * max_splits <= slots ? 4 : 1;
+  const size_t slots = (size_t)kDecodeCus * decode_waves_per_cu(head_dim);
+  return sat_mul(sat_mul((size_t)batch, (size_t)(n_heads_q / g)), (size_t)max_splits) <= slots
+             ? 4 : 1;
 }
 
 FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int head_dim,
@@ -834,16 +835,16 @@ FusedLayout decode_fused_layout(int batch, int n_heads_q, int n_heads_kv, int he
   const int g = decode_heads_per_wave(n_heads_q / n_heads_kv, batch, n_heads_q, head_dim,
                                       max_splits);
   f.waves = decode_fused_waves(batch, n_heads_q, n_heads_kv, head_dim, max_splits);
-  f.max_wg = (max_splits + f.waves - 1) / f.waves;
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  f.max_wg = (int)(((int64_t)max_splits + f.waves - 1) / f.waves);
   // The counters sit in a fixed region at the start, whatever the shape, so a
   // workspace can serve calls of different shapes: no call's partials ever
   // land where another shape keeps its (zero between calls) counters.
   f.counters = 0;
   f.n_counters = (int64_t)batch * (n_heads_q / g);
   f.wg_lse = kFusedCounterBytes;
-  f.wg_o = f.wg_lse + up((size_t)batch * n_heads_q * f.max_wg * sizeof(float));
-  f.total = f.wg_o + up((size_t)batch * n_heads_q * f.max_wg * head_dim * sizeof(float));
+  const size_t parts = sat_mul(sat_mul((size_t)batch, (size_t)n_heads_q), (size_t)f.max_wg);
+  f.wg_o = sat_add(f.wg_lse, sat_up256(sat_mul(parts, sizeof(float))));
+  f.total = sat_add(f.wg_o, sat_up256(sat_mul(parts, (size_t)head_dim * sizeof(float))));
   return f;
 }
 

@@ -6,6 +6,18 @@
 
 namespace fa {
 
+// Byte counts of workspaces: products and sums that saturate at SIZE_MAX
+// instead of wrapping, so an absurd shape can never be given a small size.
+inline size_t sat_mul(size_t a, size_t b) {
+  size_t r;
+  return __builtin_mul_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+inline size_t sat_add(size_t a, size_t b) {
+  size_t r;
+  return __builtin_add_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+inline size_t sat_up256(size_t x) { return x > SIZE_MAX - 255 ? SIZE_MAX : (x + 255) & ~(size_t)255; }
+
 // Arguments of one prefill launch (element strides; head_dim stride is 1).
 struct PrefillArgs {
   const void* q;

@@ -1075,10 +1075,11 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
 template <int D, bool BF16>
 hipError_t launch_pack_d(const PrefillArgs& a, const VtArgs& w, hipStream_t stream) {
   constexpr int BN = tile_keys(D);
-  const int ntiles = (a.seqlen_kv + BN - 1) / BN;
-  const int units = ntiles * (BN / 8) * (D / 8);
+  const int ntiles = (int)(((int64_t)a.seqlen_kv + BN - 1) / BN);   // seqlen_kv <= 2^30
+  const int64_t units = (int64_t)ntiles * (BN / 8) * (D / 8);
   hipLaunchKernelGGL((vt_pack_kernel<D, BF16>),
-                     dim3((units + kPackThreads - 1) / kPackThreads, a.n_heads_kv, a.batch),
+                     dim3((unsigned)((units + kPackThreads - 1) / kPackThreads), a.n_heads_kv,
+                          a.batch),
                      dim3(kPackThreads), 0, stream, (const unsigned short*)a.v, a.v_sb, a.v_ss, a.v_sh,
                      a.seqlen_kv, a.n_heads_kv, ntiles, (unsigned short*)w.ws);
   return hipGetLastError();
@@ -1148,20 +1149,22 @@ hipError_t launch_attn_512(const PrefillArgs& a, const VtArgs& w, bool unnorm, h
 }  // namespace
 
 size_t prefill_workspace_bytes(int batch, int seqlen_kv, int n_heads_kv, int head_dim) {
+  if (batch <= 0 || seqlen_kv <= 0 || n_heads_kv <= 0 || head_dim <= 0) return 0;
   const size_t bn = tile_keys(head_dim);
   const size_t ntiles = ((size_t)seqlen_kv + bn - 1) / bn;
-  return (size_t)batch * n_heads_kv * ntiles * bn * head_dim * 2;
+  return sat_mul(sat_mul(sat_mul((size_t)batch, (size_t)n_heads_kv), sat_mul(ntiles, bn)),
+                 (size_t)head_dim * 2);
 }
 
 SplitLayout prefill_split_layout(int batch, int seqlen_q, int n_heads_q, int head_dim) {
   SplitLayout L{};
   if (batch <= 0 || seqlen_q <= 0 || n_heads_q <= 0 || head_dim <= 0) return L;
-  const size_t blocks = (size_t)batch * n_heads_q * (((size_t)seqlen_q + 127) / 128);
-  const auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t blocks =
+      sat_mul(sat_mul((size_t)batch, (size_t)n_heads_q), ((size_t)seqlen_q + 127) / 128);
   L.cnt = 0;                      // fixed for every shape (see kSplitCounterBytes)
   L.lse = kSplitCounterBytes;
-  L.o = L.lse + up(blocks * 2 * 128 * 4);
-  L.total = L.o + blocks * 2 * 128 * (size_t)head_dim * 4;
+  L.o = sat_add(L.lse, sat_up256(sat_mul(blocks, 2 * 128 * 4)));
+  L.total = sat_add(L.o, sat_mul(sat_mul(blocks, 2 * 128 * 4), (size_t)head_dim));
   return L;
 }
 
@@ -1201,8 +1204,9 @@ int plan_units(const PlanKey& k, unsigned short* units) {
   const int D = k.head_dim;
   if (D != 64 && D != 128) return 0;
   const int bm = 128, bn = tile_keys(D);
-  const int nqb = (k.seqlen_q + bm - 1) / bm;
-  if (nqb <= 0 || nqb > 0x3fff) return 0;
+  const int64_t nqb64 = ((int64_t)k.seqlen_q + bm - 1) / bm;
+  if (nqb64 <= 0 || nqb64 > 0x3fff || k.seqlen_kv > (1 << 30)) return 0;
+  const int nqb = (int)nqb64;
   // one arrival counter per query block of every (batch entry, query head)
   if ((int64_t)k.batch * k.n_heads_q * nqb > kSplitCounters) return 0;
   // key tiles per query block, as the kernel counts them at full lengths

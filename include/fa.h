@@ -109,7 +109,9 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  *
  * Supported set: head_dim in {64, 128, 256, 512} (512: "STAGE_D.md", D1.4,
  * with the Q.K^T contraction split over a pair of waves); dtype FA_F16 or
- * FA_BF16; n_heads_q % n_heads_kv == 0; 1 <= seqlen_q <= seqlen_kv; batch >= 1;
+ * FA_BF16; n_heads_q % n_heads_kv == 0; 1 <= seqlen_q <= seqlen_kv <= 2^30;
+ * 1 <= batch, n_heads_kv <= 65535 with batch * n_heads_q * ceil(seqlen_q / 128)
+ * <= 2^30;
  * softmax_scale finite and > 0; q/k/v/o base pointers 16-byte aligned; q/k/v
  * stride_s, stride_h and stride_b multiples of 8, o strides multiples of 4;
  * k stride_s at most 2^23 elements.
@@ -297,9 +299,11 @@ uint64_t fa_prefill_workspace_size(int batch, int seqlen_kv, int n_heads_kv, int
  * merge kernels: the work items (sequence, group of query heads, split) run
  * in rounds of num_cus * (resident waves per CU), and each round lasts as long
  * as its longest split. max_splits_out = ceil(max(kv_lens) / split_len). The
- * result is a pure function of the arguments. Returns FA_ERR_INVALID_ARG for
- * null pointers, lengths < 1 or bad head counts, FA_ERR_UNSUPPORTED for an
- * unsupported head_dim.
+ * result is a pure function of the arguments (lengths beyond 4096 row blocks
+ * are planned over a thinned set of about 4096 candidate split lengths).
+ * Returns FA_ERR_INVALID_ARG for null pointers, lengths < 1 or bad head
+ * counts, FA_ERR_UNSUPPORTED for an unsupported head_dim or a length above
+ * 2^30 tokens.
  */
 int fa_decode_plan(const int32_t* kv_lens_host, int batch, int n_heads_q, int n_heads_kv,
                    int head_dim, int num_cus, int* split_len_out, int* max_splits_out);
