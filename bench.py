@@ -24,6 +24,7 @@ prefill workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import json
 import os
@@ -132,6 +133,18 @@ def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None, split=False):
         pack()
         attn()
     return run, pack, attn
+
+
+def prefill_direct_setup(torch, fa, cfg):
+    """The one-call fa_prefill_fwd for a workload, prepared (fp16 at head_dim
+    <= 128 is a single launch that reads V's rows; other inputs run the V
+    repack and the attention kernel inside the call)."""
+    from flashattention_attention_amd import inputs
+    x = inputs.make_prefill_inputs(cfg)
+    q, k, v = (_dev(torch, x[n], cfg.dtype) for n in ("q", "k", "v"))
+    return fa.prefill(q, k, v, causal=cfg.causal, softmax_scale=cfg.scale,
+                      out_unnormalized=cfg.out_unnormalized, window=cfg.window,
+                      prepare=True)
 
 
 def prefill_kernel_name(cfg, split=False):
@@ -416,6 +429,10 @@ def run_profiling_aid(torch, fa, inputs, args):
                "few_heads_split": inputs.FEW_HEADS_PREFILL}[args.only]
         _, pack, attn = prefill_setup(torch, fa, cfg, split=args.only == "few_heads_split")
         fns, label = [pack, attn], cfg.name
+    elif args.only == "prefill_f16":
+        cfg = dataclasses.replace(inputs.GQA_PREFILL, dtype="f16",
+                                  name=inputs.GQA_PREFILL.name.replace("_bf16", "_f16"))
+        fns, label = [prefill_direct_setup(torch, fa, cfg)], cfg.name
     elif args.only == "sink":
         cfg = inputs.WINDOW_PREFILL
         tens = {}
@@ -447,7 +464,8 @@ def main():
     ap.add_argument("--split-sweep", action="store_true",
                     help="also time the single-token decode at several split lengths")
     ap.add_argument("--only", choices=["prefill", "decode", "long_decode", "large_head",
-                                              "window", "hd512", "sink", "few_heads_split"],
+                                              "window", "hd512", "sink", "few_heads_split",
+                                              "prefill_f16"],
                     help="profiling aid: run only this component (warmup + steps) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="profiling aid: time a plain device-to-device copy of this many "
@@ -669,16 +687,28 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] tiny prefill", file=sys.stderr, flush=True)
         tcfg = inputs.TINY_CAUSAL          # latency-bound: one work-group, two tiles
-        t_run, t_pack, t_attn = prefill_setup(torch, fa, tcfg)
+        t_call = prefill_direct_setup(torch, fa, tcfg)   # fp16, head_dim 64: one launch
         for _ in range(20):
-            t_run()
-        r = time_calls(torch, [t_pack, t_attn], 20)
+            t_call()
+        r = time_calls(torch, [t_call], 20)
         line["prefill_tiny"] = {"workload": tcfg.name,
-                                "us_per_call": round((r[0]["median_ms"] + r[1]["median_ms"]) * 1e3, 2),
-                                "attention_us": round(r[1]["median_ms"] * 1e3, 2),
-                                "v_repack_us": round(r[0]["median_ms"] * 1e3, 2),
+                                "us_per_call": round(r[0]["median_ms"] * 1e3, 2),
+                                "launches": 1,
                                 "mflop": round(tcfg.flops() / 1e6, 3)}
-        del t_run, t_pack, t_attn
+        del t_call
+        print("[bench] GQA prefill, fp16 one-launch form", file=sys.stderr, flush=True)
+        gcfg = dataclasses.replace(inputs.GQA_PREFILL, dtype="f16",
+                                   name=inputs.GQA_PREFILL.name.replace("_bf16", "_f16"))
+        g_call = prefill_direct_setup(torch, fa, gcfg)
+        for _ in range(5):
+            g_call()
+        r = time_calls(torch, [g_call], 20)
+        gt = gcfg.flops() / (r[0]["median_ms"] * 1e-3) / 1e12
+        line["prefill_gqa_f16"] = {"workload": gcfg.name, "launches": 1,
+                                   "us_per_call": round(r[0]["median_ms"] * 1e3, 1),
+                                   "spread": r[0]["spread"], "tflops": round(gt, 2),
+                                   "frac_mfma_peak": round(gt / MI355X_BF16_DENSE_TFLOPS, 4)}
+        del g_call
         print("[bench] large-head prefill", file=sys.stderr, flush=True)
 
         hcfg = inputs.LARGE_HEAD

@@ -172,13 +172,21 @@ int fa_prefill_fwd(const void* q, int64_t q_sb, int64_t q_ss, int64_t q_sh,
                       softmax_scale, out_unnormalized);
   if (st == FA_OK) st = check_masks(fn, kv_lens, window, sink_logits);
   if (st == FA_OK) st = check_pack(fn, v, v_sb, v_ss, v_sh);
-  if (st == FA_OK)
+  // fp16 at head_dim <= 128: one launch reading V's rows, no workspace
+  const bool rows = fa::prefill_reads_v_rows(head_dim, dtype == FA_BF16);
+  if (st == FA_OK && !rows)
     st = check_workspace(fn, workspace, workspace_bytes, batch, seqlen_kv, n_heads_kv, head_dim);
+  if (st == FA_OK && rows && v_ss > (int64_t)(1 << 23))
+    st = fail(FA_ERR_UNSUPPORTED, "%s: v sequence stride above 2^23 elements", fn);
   if (st != FA_OK) return st;
   const fa::PrefillArgs a =
       prefill_args(q, q_sb, q_ss, q_sh, k, k_sb, k_ss, k_sh, v, v_sb, v_ss, v_sh, o, o_sb, o_ss,
                    o_sh, lse, row_sum, batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, causal,
                    softmax_scale, kv_lens, window, sink_logits);
+  if (rows)
+    return hip_status(fa::launch_prefill_attn_vrow(a, head_dim, out_unnormalized != 0,
+                                                   (hipStream_t)stream),
+                      "fa_prefill_fwd attention launch");
   const fa::VtArgs w{workspace, (size_t)workspace_bytes};
   const hipError_t e =
       fa::launch_prefill_pack(a, w, head_dim, dtype == FA_BF16, (hipStream_t)stream);

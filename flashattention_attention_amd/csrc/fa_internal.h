@@ -129,6 +129,11 @@ hipError_t launch_prefill_pack(const PrefillArgs& a, const VtArgs& w, int head_d
                                hipStream_t stream);
 hipError_t launch_prefill_attn(const PrefillArgs& a, const VtArgs& w, int head_dim, bool bf16,
                                bool unnormalized, hipStream_t stream);
+// One launch reading V's rows directly (no V^T workspace): fp16 inputs at
+// head_dim 64 or 128, where prefill_reads_v_rows is true.
+bool prefill_reads_v_rows(int head_dim, bool bf16);
+hipError_t launch_prefill_attn_vrow(const PrefillArgs& a, int head_dim, bool unnormalized,
+                                    hipStream_t stream);
 // The same with the key split (sp.n_units > 0); head_dim 64 or 128, normalized output.
 hipError_t launch_prefill_attn_split(const PrefillArgs& a, const VtArgs& w, const SplitPlan& sp,
                                      int head_dim, bool bf16, hipStream_t stream);

@@ -290,10 +290,14 @@ struct NoSplit {};
 template <bool SPLIT> struct SplitArg { using type = NoSplit; };
 template <> struct SplitArg<true> { using type = SplitPlan; };
 
-template <int D, bool BF16, bool UNNORM, int HP, bool SPLIT>
+// VROW: V tiles come straight from V's rows by DMA (fp16 only, head_dim <= 128)
+// and each P.V operand is assembled from two LDS transpose reads, so no V^T
+// pre-pass runs; otherwise they come from the V^T tiles the pre-pass wrote.
+template <int D, bool BF16, bool UNNORM, int HP, bool SPLIT, bool VROW = false>
 __global__ void __launch_bounds__(64 * wg_waves(D, HP)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
                typename SplitArg<SPLIT>::type sp) {
+  static_assert(!VROW || (!BF16 && D <= 128), "V rows are read directly for fp16, head_dim <= 128");
   constexpr int kWaves = wg_waves(D, HP);
   constexpr bool PIPE = D <= 128;            // software-pipelined loop (register budget)
   constexpr int QG = 4;                      // query groups of 32 rows per head
@@ -314,6 +318,11 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   constexpr int K_INSTR = KT / 1024 / kWaves;   // DMA instructions per wave per tile
   constexpr int V_INSTR = VT / 1024 / kWaves;
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile too small for the DMA split");
+  // Row swizzle of V rows in LDS (VROW): one transpose read takes 64 bytes
+  // (4 chunks) from each of 4 consecutive rows; XOR-ing the chunk index with
+  // 4 * (row & 3) (256-byte rows) or 4 * ((row >> 1) & 1) (128-byte rows, two
+  // per bank line) puts the four rows on distinct banks.
+  constexpr auto vswz = [](int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); };
 
   // K/V^T tiles (two stages); after the loop, the per-wave O staging area
   // (32 rows x D / OH fp32 per wave).
@@ -393,6 +402,8 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   const unsigned short* kp =
       (const unsigned short*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
   const char* vtp = (const char*)vt_ws + ((int64_t)b * a.n_heads_kv + hk) * ntiles_all * VT;
+  const unsigned short* vp =
+      (const unsigned short*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
 
   const unsigned lds_base = (unsigned)(uintptr_t)(lptr_t)lds;
 
@@ -431,6 +442,37 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
     }
   };
   auto issue_v = [&](int t, unsigned dst) {
+    if constexpr (VROW) {
+      // V rows as K rows (same tile size, RPI rows per 1 KB DMA instruction);
+      // lane p of an instruction stores its row's 16-byte chunk (p % CPR) ^
+      // vswz(row) at position p, where vswz spreads the four rows that one
+      // transpose read touches over distinct banks. The swizzle depends on the
+      // row only through its offset inside the instruction, so the lane part of
+      // the address is the same for every instruction of the tile.
+      const int t0 = (tb + t) * BN;
+      unsigned ln = (unsigned)lane;
+      asm volatile("" : "+v"(ln));
+      const unsigned lrow = ln / CPR;
+      const unsigned lc16 = ((ln % CPR) ^ (unsigned)vswz((int)lrow)) << 4;
+      if (t0 + BN <= a.seqlen_kv) {
+        const unsigned lrow_b = lrow * (unsigned)a.v_ss * 2u;   // < 2^31 (v_ss <= 2^23)
+#pragma unroll
+        for (int j = 0; j < V_INSTR; ++j) {
+          const int r0 = (wave * V_INSTR + j) * RPI;
+          dma16_at(vp + (int64_t)(t0 + r0) * a.v_ss, lc16 + lrow_b,
+                   lds_base + dst + (wave * V_INSTR + j) * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < V_INSTR; ++j) {
+          const int r0 = (wave * V_INSTR + j) * RPI;
+          const int key = min(t0 + r0 + (int)lrow, a.seqlen_kv - 1);   // P = 0 past the end
+          dma16((const char*)(vp + (int64_t)key * a.v_ss) + lc16,
+                lds_base + dst + (wave * V_INSTR + j) * 1024);
+        }
+      }
+      return;
+    }
     const char* base = vtp + (int64_t)(tb + t) * VT;
     unsigned ln = (unsigned)lane;
     asm volatile("" : "+v"(ln));
@@ -455,6 +497,21 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     va_off[ks] = vt_chunk_offset<BN>(n, ks * 2 + hh);
+  // VROW: the byte offset, in a V-row stage, of this lane's first transpose read
+  // for head-dim block db at k-step 0. Lane j of a 16-lane group g points at
+  // the 4 dims m0 + 4 (j % 4) .. + 3 (m0 = 32 db + 16 (g & 1)) of key 4 hh +
+  // j / 4: the read then hands lane j dim m0 + j of keys 4 hh + 0..3, and a
+  // second read 8 keys further the keys 8 + 4 hh + 0..3, the key order of P.
+  int vr_off[NDB];
+  if constexpr (VROW) {
+    const int g = lane >> 4, j = lane & 15;
+    const int key = 4 * hh + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int chunk = 4 * db + 2 * (g & 1) + ((j & 3) >> 1);
+      vr_off[db] = key * KROW + ((chunk ^ vswz(key)) << 4) + 8 * (j & 1);
+    }
+  }
 
   float m_used = -1e30f;   // base of the exponentials (log2 units)
   float m_true = -1e30f;   // exact running row max (log2 units)
@@ -546,9 +603,23 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        oacc[db] = mfma_pv(*(const u32x4*)(vst + va_off[ks] + db * 32 * (BN * 2)), pk[ks],
-                           oacc[db]);
+      for (int db = 0; db < NDB; ++db) {
+        u32x4 va;
+        if constexpr (VROW) {
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+          const char* p0 = vst + vr_off[db] + ks * 16 * KROW;   // keys 16 ks + 4 hh + 0..3
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lptr_t)p0);
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lptr_t)(p0 + 8 * KROW));
+          const auto l2 = __builtin_bit_cast(f32x2, lo), h2 = __builtin_bit_cast(f32x2, hi);
+          va = u32x4{__float_as_uint(l2[0]), __float_as_uint(l2[1]), __float_as_uint(h2[0]),
+                     __float_as_uint(h2[1])};
+        } else {
+          va = *(const u32x4*)(vst + va_off[ks] + db * 32 * (BN * 2));
+        }
+        oacc[db] = mfma_pv(va, pk[ks], oacc[db]);
+      }
   };
   // Every wave computes every tile of the block, including key halves that
   // lie wholly above its queries (they come out as P = 0): all waves meet at
@@ -608,12 +679,13 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       tm = row_max(nxt);
       {
         // P.V: V^T operand reads four MFMAs ahead; the max's VALU among them.
-        constexpr int NP = NKS * NDB, AHEAD = 4;
-        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 1);
+        // (From V rows an operand takes two transposing reads.)
+        constexpr int NP = NKS * NDB, AHEAD = 4, RD = VROW ? 2 : 1;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * RD, 1);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          if (i + AHEAD < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+          if (i + AHEAD < NP) __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
         }
       }
@@ -1112,6 +1184,29 @@ hipError_t launch_attn_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hip
   return hipGetLastError();
 }
 
+// The attention launch reading V's rows directly (fp16, head_dim <= 128).
+template <int D>
+hipError_t launch_attn_vrow_d(const PrefillArgs& a, bool unnorm, hipStream_t stream) {
+  constexpr int BM = block_rows(D);
+  const int per_group = a.n_heads_q / a.n_heads_kv;
+  const int nqb = (a.seqlen_q + BM - 1) / BM;
+  const auto go = [&](auto hp_c) {
+    constexpr int HP = decltype(hp_c)::value;
+    const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
+    if (unnorm)
+      hipLaunchKernelGGL((prefill_kernel<D, false, true, HP, false, true>), grid,
+                         dim3(64 * wg_waves(D, HP)), 0, stream, a, nullptr, NoSplit{});
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, false, false, HP, false, true>), grid,
+                         dim3(64 * wg_waves(D, HP)), 0, stream, a, nullptr, NoSplit{});
+  };
+  if (per_group % 2 == 0)
+    go(std::integral_constant<int, 2>{});
+  else
+    go(std::integral_constant<int, 1>{});
+  return hipGetLastError();
+}
+
 template <int D, bool BF16>
 hipError_t launch_split_d(const PrefillArgs& a, const VtArgs& w, const SplitPlan& sp,
                           hipStream_t stream) {
@@ -1336,6 +1431,17 @@ hipError_t launch_prefill_pack(const PrefillArgs& a, const VtArgs& w, int head_d
     case 128: return bf16 ? launch_pack_d<128, true>(a, w, stream) : launch_pack_d<128, false>(a, w, stream);
     case 256: return bf16 ? launch_pack_d<256, true>(a, w, stream) : launch_pack_d<256, false>(a, w, stream);
     case 512: return bf16 ? launch_pack_d<512, true>(a, w, stream) : launch_pack_d<512, false>(a, w, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool prefill_reads_v_rows(int head_dim, bool bf16) { return !bf16 && head_dim <= 128; }
+
+hipError_t launch_prefill_attn_vrow(const PrefillArgs& a, int head_dim, bool unnormalized,
+                                    hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_attn_vrow_d<64>(a, unnormalized, stream);
+    case 128: return launch_attn_vrow_d<128>(a, unnormalized, stream);
     default: return hipErrorInvalidValue;
   }
 }

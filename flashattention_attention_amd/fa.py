@@ -230,7 +230,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
             row_sum: Optional[torch.Tensor] = None, want_row_sum: bool = False,
             workspace: Optional[torch.Tensor] = None, kv_lens: Optional[torch.Tensor] = None,
             window: int = 0, sink_logits: Optional[torch.Tensor] = None,
-            split_workspace: Optional[torch.Tensor] = None):
+            split_workspace: Optional[torch.Tensor] = None, prepare: bool = False):
     """Attention forward. q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (fp16/bf16, D contiguous).
 
     ``kv_lens`` (optional int32 GPU tensor [B]) hides keys j >= kv_lens[b];
@@ -240,14 +240,17 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
     sink term exp(sink) with no value row to every row's softmax.
 
     ``workspace`` (optional) is a uint8 GPU tensor of at least
-    ``prefill_workspace_size(...)`` bytes; one is allocated when omitted.
+    ``prefill_workspace_size(...)`` bytes; one is allocated when omitted, except
+    for fp16 inputs at head_dim <= 128, which need none (one launch reads V's
+    rows directly).
     ``split_workspace`` (optional, zero-filled before its first use): run as
     prefill_pack_v + prefill_packed with the key split of the longest query
     blocks (see prefill_packed).
 
     Returns (o, lse) or (o, lse, row_sum) when ``out_unnormalized`` or
     ``want_row_sum``; o is fp32 [B,Sq,Hq,D] (un-normalized when asked), lse and
-    row_sum are fp32 [B,Hq,Sq].
+    row_sum are fp32 [B,Hq,Sq]. With prepare=True (not with split_workspace),
+    returns a callable that repeats the call into the same outputs instead.
     """
     dev = _on_gpu(q, k, v)
     if v.dim() != 4 or k.shape != v.shape or v.dtype != k.dtype:
@@ -261,24 +264,33 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
     scale = _default_scale(D) if softmax_scale is None else float(softmax_scale)
     kv_lens, window = _masks(kv_lens, window, B, dev)
     sink_logits = _sinks(sink_logits, Hq, dev)
-    workspace = _workspace(k, dev, workspace)
+    # fp16 at head_dim <= 128 reads V's rows directly (one launch, no workspace)
+    direct = q.dtype == torch.float16 and D <= 128 and split_workspace is None
+    if not direct or workspace is not None:
+        workspace = _workspace(k, dev, workspace)
     if split_workspace is not None:
+        if prepare:
+            raise FAError("prepare=True is not offered with split_workspace")
         prefill_pack_v(v, workspace)
         return prefill_packed(q, k, workspace, causal=causal, softmax_scale=scale,
                               out_unnormalized=out_unnormalized, out=out, lse=lse,
                               row_sum=row_sum, want_row_sum=want_row_sum, kv_lens=kv_lens,
                               window=window, sink_logits=sink_logits,
                               split_workspace=split_workspace)
-    st = load_library().fa_prefill_fwd(
-        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
-        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
-        v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
-        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
-        lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
-        B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
-        1 if out_unnormalized else 0, _ptr(kv_lens), window, _ptr(sink_logits),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(st, "fa_prefill_fwd")
+    args = (q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+            k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+            v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
+            out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+            lse.data_ptr(), row_sum.data_ptr() if row_sum is not None else None,
+            B, Sq, Skv, Hq, Hkv, D, _dtype_code(q), 1 if causal else 0, scale,
+            1 if out_unnormalized else 0, _ptr(kv_lens), window, _ptr(sink_logits),
+            workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+            _stream(dev))
+    keep = (q, k, v, out, lse, row_sum, kv_lens, sink_logits, workspace)
+    call = _issue("fa_prefill_fwd", args, keep, prepare)
+    if prepare:
+        return call
     return (out, lse, row_sum) if need_rs else (out, lse)
 
 

@@ -103,9 +103,13 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  *
  * workspace: caller-owned device scratch of at least
  * fa_prefill_workspace_size(batch, seqlen_kv, n_heads_kv, head_dim) bytes,
- * 256-byte aligned. The call first repacks V into it (fp16, transposed per
- * key tile), then runs the attention kernel; its contents are undefined
- * afterwards and it must not be shared by calls that overlap in time.
+ * 256-byte aligned. For bf16 inputs, and fp16 inputs at head_dim 256 and 512,
+ * the call first repacks V into it (fp16, transposed per key tile), then runs
+ * the attention kernel; its contents are undefined afterwards and it must not
+ * be shared by calls that overlap in time. fp16 inputs at head_dim 64 and 128
+ * take one launch that reads V's rows in place (transposing loads from LDS):
+ * workspace and workspace_bytes are then ignored and may be NULL and 0, and
+ * v stride_s must be at most 2^23 elements, as k's.
  *
  * Supported set: head_dim in {64, 128, 256, 512} (512: "STAGE_D.md", D1.4,
  * with the Q.K^T contraction split over a pair of waves); dtype FA_F16 or

@@ -108,7 +108,12 @@ def _prefill(**kw):
     (dict(scale=-1.0), 1), (dict(q=ALIGNED + 2), 1), (dict(o=ALIGNED + 4), 1),
     (dict(qs=(128 * 4 * 128, 4 * 128 + 4, 128)), 1), (dict(os=(128, 2, 128)), 1),
     (dict(ks=(-8, 256, 128)), 1), (dict(Sq=2**31 - 1, Skv=2**31 - 1, Hq=128), 2),
-    (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(ws=ALIGNED + 16), 1),
+    # bf16 (and fp16 at head_dim 256) run the V repack: the workspace is checked
+    (dict(ws=None, dtype=1), 1), (dict(wsb=1000, dtype=1), 1), (dict(ws=ALIGNED + 16, dtype=1), 1),
+    (dict(ws=None, D=256), 1),
+    # fp16 at head_dim <= 128 reads V's rows: no workspace needed; the call passes
+    # its host checks and fails only at the launch (no GPU here)
+    (dict(ws=None, wsb=0), 3), (dict(ws=None, wsb=0, D=64), 3),
     (dict(win=-1), 1), (dict(lens=ALIGNED + 2), 1), (dict(sink=ALIGNED + 2), 1),
 ])
 def test_prefill_validation(kw, status):

@@ -50,10 +50,14 @@ def test_prefill_kernels_run_two_waves_without_scratch():
     ks = _pick(rep, "prefill_kernelILi64E", "prefill_kernelILi128E", "prefill_kernelILi256E",
                "prefill512_kernel")
     # head_dim 64 and 128: {bf16, fp16} x {normalized, un-normalized} x {1, 2 heads},
-    # plus the key-split form ({bf16, fp16} x {1, 2 heads}, normalized);
+    # plus the key-split form ({bf16, fp16} x {1, 2 heads}, normalized) and the
+    # fp16 form that reads V's rows ({normalized, un-normalized} x {1, 2 heads});
     # head_dim 256 and 512: {bf16, fp16} x {normalized, un-normalized}
-    assert len(ks) == 32, sorted(ks)
-    assert len([k for k in ks if "Lb1EEEvNS" in k and "prefill_kernel" in k]) == 8, sorted(ks)
+    # (template arguments: D, bf16, un-normalized, heads, split, V rows)
+    assert len(ks) == 40, sorted(ks)
+    assert len([k for k in ks if "ELb1ELb0EEEvNS" in k]) == 8, sorted(ks)
+    vrow = [k for k in ks if "ELb0ELb1EEEvNS" in k]
+    assert len(vrow) == 8 and all("ILi64ELb0E" in k or "ILi128ELb0E" in k for k in vrow), vrow
     for name, r in ks.items():
         assert r["scratch_bytes"] == 0 and r["vgpr_spill"] == 0, (name, r)
         assert r["waves_per_simd"] == 2, (name, r)
