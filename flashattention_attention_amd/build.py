@@ -27,6 +27,11 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip", "fa_merge.hip"]
 ARCH = "gfx950"
+# Per-source flags. The decode kernels keep their MFMA accumulators in VGPRs
+# (the AGPR form made the register allocator copy every accumulator between
+# the two files on each block, which cost the multi-head decode its second
+# wave per SIMD).
+EXTRA = {"fa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -77,7 +82,7 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
         obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
         hip = src.endswith(".hip")
         lang = ["-x", "hip"] if hip else []
-        extra = ["-Rpass-analysis=kernel-resource-usage"] if hip else []
+        extra = (["-Rpass-analysis=kernel-resource-usage"] if hip else []) + EXTRA.get(src, [])
         cmd = [hipcc()] + compile_flags() + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -22,10 +22,12 @@
 //    reduced with DPP row permutes, and the online-softmax update is done
 //    once per block and head (section 3.2 of the same page gives the per-row
 //    form: new max, correction factor, exponential, running sum and output);
-//  * from 5 query heads per wave (head_dim <= 128) the per-head dot products
-//    and exponentials outweigh the loads, and Q.K^T moves to the matrix
-//    cores (split_attend_mfma): each K row then serves up to 16 heads in one
-//    16x16x32 MFMA, and the exponentials are spread one per (key, head).
+//  * with several query heads per wave (head_dim <= 128) the per-head work
+//    outweighs the loads and moves to the matrix cores: for fp16 caches from
+//    4 heads per wave both Q.K^T and P.V (split_attend_mfma_pv), for bf16
+//    from 5 heads Q.K^T only (split_attend_mfma); each K row then serves up
+//    to 16 heads in one 16x16x32 MFMA, and the exponentials are spread one
+//    per (key, head).
 //
 // Each split emits a normalized partial O_s and its natural-log LSE_s. The
 // merge then combines the partials by LSE in a fixed order, so the result is
@@ -105,6 +107,13 @@ __device__ __forceinline__ float half_hi(unsigned w) {
 }
 
 constexpr int lanes_per_row(int d) { return d >= 128 ? 16 : 8; }
+
+// Two floats to packed fp16 (round to nearest even).
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  f32x2v v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
+}
 
 // Online softmax of query heads h0 .. h0+G-1 of sequence b over its keys
 // [lo, hi) (lo < hi), by one wave. D: head_dim. G: query heads served per wave
@@ -266,10 +275,11 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Used from 5 heads per wave: there the VALU form is bound by its per-head
-// dot products and exponentials (at 32 cached keys per block, 4 KV heads and
-// 28 or 32 query heads the matrix-core form is 1.3-1.4x faster); at 3 and 4
-// heads both forms reach the same HBM rate and the VALU one is the leaner.
+// Q.K^T on the matrix cores from 5 heads per wave: there the VALU form is
+// bound by its per-head dot products and exponentials (at 32 cached keys per
+// block, 4 KV heads and 28 or 32 query heads this form was 1.3-1.4x faster);
+// at 3 and 4 heads both reached the same HBM rate. fp16 caches take the form
+// with P.V on the matrix cores as well (decode_pv_on_mfma), from 4 heads.
 __host__ __device__ constexpr bool decode_uses_mfma(int d, int g) { return d <= 128 && g >= 5; }
 
 template <int D, int G, bool BF16>
@@ -430,13 +440,258 @@ __device__ __forceinline__ void split_attend_mfma(const DecodeArgs& a, int b, in
   }
 }
 
-// The split of one wave by whichever form serves its (D, G); pw is used by
-// the matrix-core form only.
+// The same split with P.V on the matrix cores as well (fp16 caches, D <= 128).
+// Per 32-key block:
+//  * K and V rows are loaded as whole rows (16 lanes x 16 bytes per 256-byte
+//    row, like the VALU form): the MFMA operand layout would have each load
+//    instruction take 64 bytes from each of 16 rows, which streamed ~10 %
+//    slower from HBM. The wave stores both blocks to its LDS area (16-byte
+//    chunks XOR-swizzled by row) and reads the operands back from there;
+//  * S^T = K . Q^T as in split_attend_mfma (16 keys x 16 heads per
+//    v_mfma_f32_16x16x32_f16; K read as lane l: row l % 16 of the half,
+//    chunk 4*kk + l / 16), then the block max and the exponentials, one per
+//    (key, head);
+//  * P^T is already the B operand of O^T = V^T . P^T (heads along N): lane l
+//    holds P of head l % 16 for keys 4*(l/16) + 0..3 of both 16-key halves,
+//    and the MFMA's 32-long contraction takes those 8 keys in that order;
+//  * the V^T operand comes from two ds_read_b64_tr_b16, which hand lane l
+//    dim 16*db + l % 16 of keys 4*(l/16) + 0..3 and of the same keys 16
+//    further;
+//  * O^T accumulates in the MFMA's C layout (lane l: dims 16*db + 4*(l/16) +
+//    0..3 of head l % 16), so the rescale on a new max is lane-local.
+// P enters the MFMA as fp16 with 2^kPShift headroom over the running max (so
+// the small weights stay normal); l sums the fp32 weights. At the end O^T goes
+// through LDS to the row layout of split_attend's contract.
+// lw: this wave's LDS scratch, 2 x 32 x D halves (K block, V block; 256-byte aligned).
+constexpr float kPShift = 6.0f;   // P <= 2^(kSlack + kPShift) = 16384 in fp16
+
+__host__ __device__ constexpr bool decode_pv_on_mfma(int d, int g, bool bf16) {
+  return !bf16 && d <= 128 && g >= 4;
+}
+
+template <int D, int G>
+__device__ __forceinline__ void split_attend_mfma_pv(const DecodeArgs& a, int b, int h0, int lo,
+                                                     int hi, int lane, char* lw, float (&m)[G],
+                                                     float (&l)[G],
+                                                     float (&o)[G][D / lanes_per_row(D)]) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static_assert(G >= 1 && G <= 16, "at most 16 heads per wave");
+  constexpr int LPK = lanes_per_row(D);    // lanes per row (row layout)
+  constexpr int EPL = D / LPK;             // 8: one 16-byte chunk per lane
+  static_assert(EPL == 8, "one chunk per lane and row");
+  constexpr int KPS = 64 / LPK;            // rows per load step
+  constexpr int BK = 32;                   // keys per block
+  constexpr int NB = BK / KPS;             // load steps per block
+  constexpr int NKK = D / 32;              // Q.K^T k-steps
+  constexpr int NDB = D / 16;              // 16-dim blocks of O^T
+  constexpr int ROWB = D * 2;              // bytes per row in LDS
+  constexpr int BLK = BK * ROWB;           // bytes per block in LDS
+  // Chunk swizzles by row r. K: the 16 rows one operand read touches, 4
+  // chunks each, fill every chunk position of the bank lines 4 times (the
+  // minimum for 1 KB). V: the 16 rows one transpose read touches, 2 chunks
+  // each, land on distinct chunk pairs of their bank line (2 passes for 512 B).
+  constexpr auto kswz = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  constexpr auto vswz = [](int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+
+  const int hk = h0 / (a.n_heads_q / a.n_heads_kv);
+  const int slot = lane / LPK;
+  const int c = lane % LPK;
+  const int n = lane & 15;                 // MFMA column: query head h0 + n
+  const int quad = lane >> 4;
+
+  u32x4 qop[NKK];
+  {
+    const unsigned short* qp = (const unsigned short*)a.q + (int64_t)b * a.q_sb +
+                               (int64_t)(h0 + min(n, G - 1)) * a.q_sh + quad * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qop[kk] = n < G ? *(const u32x4*)(qp + kk * 32) : u32x4{0, 0, 0, 0};
+  }
+
+  const int64_t row0 = a.kv_offsets[b];
+  const int64_t head = row0 * a.kv_st + (int64_t)hk * a.kv_sh + c * EPL;
+  const unsigned short* kbase = (const unsigned short*)a.k + head;
+  const unsigned short* vbase = (const unsigned short*)a.v + head;
+
+  // LDS byte offsets. Writes: this lane's chunk of load step j (row
+  // j*KPS + slot); the swizzles of those rows depend on j only through
+  // j's parity for V at D = 128. Reads: K operand of half sb and k-step kk
+  // (row 16*sb + n, chunk 4*kk + quad); V^T transpose read of dim block db
+  // (row 4*quad + (lane % 16) / 4, dims 16*db + 4*(lane % 4) .. +3).
+  const unsigned kl = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lw;
+  const unsigned vl = kl + BLK;
+  const unsigned kw_off = kl + (unsigned)(slot * ROWB + ((c ^ kswz(slot)) << 4));
+  unsigned vw_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    vw_off[par] = vl + (unsigned)(slot * ROWB + ((c ^ vswz(par * KPS + slot)) << 4));
+  // The area is 256-byte aligned and the swizzles only flip the bits that
+  // select 64-byte (K) or 32-byte (V) groups of a row, so k-step kk and dim
+  // block db are reached from the kk = 0 / db = 0 offsets by an XOR.
+  const unsigned kr0 = kl + (unsigned)(n * ROWB + ((quad ^ kswz(n)) << 4));
+  unsigned vr0;
+  {
+    const int j = lane & 15;
+    const int r = 4 * quad + (j >> 2);
+    vr0 = vl + (unsigned)(r * ROWB + ((((j & 3) >> 1) ^ vswz(r)) << 4) + 8 * (j & 1));
+  }
+
+  // One block of K and V rows (rows past hi repeat row hi-1, valid memory;
+  // their scores are masked).
+  auto load_block = [&](int start, u32x4 (&kd)[NB], u32x4 (&vd)[NB]) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int64_t off = (int64_t)min(start + j * KPS + slot, hi - 1) * a.kv_st;
+      kd[j] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
+      vd[j] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
+    }
+  };
+
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+  float mc = -1e30f;   // running max (log2 units) of head column n
+  float lp = 0.0f;     // this lane's part of head n's row sum (relative to mc - kPShift)
+  f32x4 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // A block's rows to LDS. (The previous block's operand reads were consumed
+  // by its MFMAs, so this wave's LDS operations have drained.)
+  auto stage_block = [&](const u32x4 (&kd)[NB], const u32x4 (&vd)[NB]) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      *(lds_u32x4*)(uintptr_t)(kw_off + (unsigned)(j * KPS * ROWB)) = kd[j];
+      *(lds_u32x4*)(uintptr_t)(vw_off[(j * KPS / 4) & 1] + (unsigned)(j * KPS * ROWB)) = vd[j];
+    }
+  };
+  auto compute_block = [&](int start) {
+    // Every lane's rows have landed before any lane reads them.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    f32x4 s[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        s[sb] = mfma16<false>(
+            *(const lds_u32x4*)(uintptr_t)((kr0 ^ (unsigned)(kk << 6)) + (unsigned)(sb * 16 * ROWB)),
+            qop[kk], s[sb]);
+    }
+    if (start + BK > hi) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (start + sb * 16 + quad * 4 + i >= hi) s[sb][i] = -INFINITY;
+    }
+    float lm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    lm = fmaxf(lm, __shfl_xor(lm, 16));
+    lm = fmaxf(lm, __shfl_xor(lm, 32));
+    const float bm = lm * a.scale_log2;    // the max commutes with the positive scale
+    const bool grow = bm > mc + kSlack;
+    if (__ballot(grow)) {
+      const float nm = grow ? bm : mc;
+      const float corr = __builtin_amdgcn_exp2f(mc - nm);
+      mc = nm;
+      lp *= corr;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[db][i] *= corr;
+    }
+    const float base = mc - kPShift;
+    float p[2][4];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[sb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], a.scale_log2, -base));
+        lp += p[sb][i];
+      }
+    const u32x4 pb = u32x4{pack_f16x2(p[0][0], p[0][1]), pack_f16x2(p[0][2], p[0][3]),
+                           pack_f16x2(p[1][0], p[1][1]), pack_f16x2(p[1][2], p[1][3])};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const unsigned vr = vr0 ^ (unsigned)(db << 5);
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)vr);
+      const s16x4 hi4 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(vr + 16 * ROWB));
+      const f32x2 l2 = __builtin_bit_cast(f32x2, lo4), h2 = __builtin_bit_cast(f32x2, hi4);
+      const u32x4 va = u32x4{__float_as_uint(l2[0]), __float_as_uint(l2[1]),
+                             __float_as_uint(h2[0]), __float_as_uint(h2[1])};
+      oacc[db] = mfma16<false>(va, pb, oacc[db]);
+    }
+  };
+
+  // Two register buffers in turn, two blocks ahead: once a block's rows are in
+  // LDS its registers take the block after next, so while a block is computed
+  // the next two are in flight. The loads are issued unconditionally (past hi
+  // they repeat row hi-1 and go unused): the compiler can then wait for
+  // exactly the block it stages instead of for every load in flight.
+  u32x4 ka[NB], kb[NB], va[NB], vb[NB];
+  load_block(lo, ka, va);
+  load_block(lo + BK, kb, vb);
+  for (int start = lo;; start += 2 * BK) {
+    stage_block(ka, va);
+    load_block(start + 2 * BK, ka, va);
+    compute_block(start);
+    if (start + BK >= hi) break;
+    stage_block(kb, vb);
+    load_block(start + 3 * BK, kb, vb);
+    compute_block(start + BK);
+    if (start + 2 * BK >= hi) break;
+  }
+
+  // Head n's row sum over the four lane groups; m and l of every head to every lane.
+  lp += __shfl_xor(lp, 16);
+  lp += __shfl_xor(lp, 32);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mc), g)) - kPShift;
+    l[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp), g));
+  }
+  // O^T (C layout) -> [head][dim] fp32 in LDS -> row layout (every slot alike).
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the last block's reads are done
+  float* ob = (float*)lw;                                // G x D floats fit in 32 x D halves
+  if (n < G) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *(f32x4*)(ob + n * D + db * 16 + quad * 4) = oacc[db];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const f32x4 x0 = *(const f32x4*)(ob + g * D + c * EPL);
+    const f32x4 x1 = *(const f32x4*)(ob + g * D + c * EPL + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[g][e] = x0[e];
+      o[g][4 + e] = x1[e];
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the area is reused
+}
+
+// LDS floats per wave that split_run needs: the K and V blocks of the form with
+// P.V on the matrix cores, the P buffer of the form with Q.K^T only, else none.
+__host__ __device__ constexpr int decode_lds_floats(int d, int g, bool bf16) {
+  return decode_pv_on_mfma(d, g, bf16) ? 2 * 32 * d / 2
+                                       : (decode_uses_mfma(d, g) ? kPRows * kPStride : 1);
+}
+
+// The split of one wave by whichever form serves its (D, G); pw (this wave's
+// decode_lds_floats floats of LDS) is used by the matrix-core forms only.
 template <int D, int G, bool BF16>
 __device__ __forceinline__ void split_run(const DecodeArgs& a, int b, int h0, int lo, int hi,
                                          int lane, float* pw, float (&m)[G], float (&l)[G],
                                          float (&o)[G][D / lanes_per_row(D)]) {
-  if constexpr (decode_uses_mfma(D, G))
+  if constexpr (decode_pv_on_mfma(D, G, BF16))
+    split_attend_mfma_pv<D, G>(a, b, h0, lo, hi, lane, (char*)pw, m, l, o);
+  else if constexpr (decode_uses_mfma(D, G))
     split_attend_mfma<D, G, BF16>(a, b, h0, lo, hi, lane, pw, m, l, o);
   else
     split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
@@ -459,7 +714,7 @@ decode_partial_kernel(DecodeArgs a) {
   const int hi = min(L, lo + a.split_len);
   const int slot = lane / LPK;
   const int c = lane % LPK;
-  __shared__ __attribute__((aligned(16))) float pbuf[decode_uses_mfma(D, G) ? kPRows * kPStride : 1];
+  __shared__ __attribute__((aligned(256))) float pbuf[decode_lds_floats(D, G, BF16)];
   float m[G], l[G], o[G][EPL];
   split_run<D, G, BF16>(a, b, h0, lo, hi, lane, pbuf, m, l, o);
   if (slot == 0) {
@@ -561,8 +816,13 @@ decode_merge_kernel(MergeArgs a) {
 // (an agent-scope counter; no work-group ever waits for another) merges those
 // partials in index order and resets the counter to zero. The result is a
 // fixed function of the split plan, so repeated runs are byte-identical.
+// The one-wave matrix-core P.V form is held to two waves per SIMD (left to
+// itself, the allocator moved a few registers to AGPRs and halved it). The
+// 4-wave form runs only when the whole call fits in one round of resident
+// waves, where occupancy matters less; held to two waves it spills.
 template <int D, int G, bool BF16, int NW>
 __global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(decode_pv_on_mfma(D, G, BF16) && NW == 1 ? 2 : 1)))
 decode_fused_kernel(DecodeArgs a) {
   constexpr int LPK = lanes_per_row(D);
   constexpr int EPL = D / LPK;
@@ -570,7 +830,7 @@ decode_fused_kernel(DecodeArgs a) {
   __shared__ float so[NW][G][D];
   __shared__ float sm[NW][G], sl[NW][G];
   __shared__ int is_last;
-  __shared__ __attribute__((aligned(16))) float pbuf[NW][decode_uses_mfma(D, G) ? kPRows * kPStride : 1];
+  __shared__ __attribute__((aligned(256))) float pbuf[NW][decode_lds_floats(D, G, BF16)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hg = blockIdx.x, h0 = hg * G, y = blockIdx.y, b = blockIdx.z;

@@ -293,10 +293,12 @@ def test_decode_lengths_and_empty_splits(torch_gpu, dtype, D, hq, hkv):
                         scale=scale, dtype=dtype)
     assert np.abs(o - ref["o"]).max() <= O_TOL
     assert np.abs(lse - ref["lse"]).max() <= LSE_TOL
-    # one visible key: the output is that key's V row
+    # one visible key: the output is that key's V row, up to the rounding of
+    # its weight (fp16 into the matrix-core P.V against the fp32 row sum:
+    # < 1.5e-6 relative, see test_decode_mfma_gpu)
     hk_of = np.arange(hq) // (hq // hkv)
     v0 = inputs.half_bits_to_f32(x["v_cache"][0], dtype)[hk_of]
-    np.testing.assert_allclose(o[0], v0, atol=1e-6, rtol=0)
+    np.testing.assert_allclose(o[0], v0, atol=1e-6, rtol=4e-6)
 
 
 def test_decode_bad_lengths_give_nan(torch_gpu):
