@@ -3,8 +3,9 @@
 One step = one pass of the whole hot path on one model shape (28 query heads,
 4 KV heads, head_dim 128): the causal GQA prefill of a 3314-token prompt (bf16)
 followed by a single-token split-KV decode against a 1641-token fp16 KV cache
-(split partials + LSE merge). Inputs are synthetic N(0,1) draws, resident in
-HBM before the timed region.
+(split partials and their LSE merge, in one launch; the two-launch form is
+reported beside it). Inputs are synthetic N(0,1) draws, resident in HBM
+before the timed region.
 
 Prints one JSON line. ``value`` is the prefill's algorithmic throughput in
 TFLOP/s (4 * head_dim FLOPs per visible query/key pair, per query head) over
@@ -493,11 +494,11 @@ def main():
 
     prefill, p_pack, p_attn = prefill_setup(torch, fa, pcfg)
     d_partial, d_merge, dinfo = decode_setup(torch, fa, dcfg)
+    d_fused = dinfo["fused"]       # split partials and their merge in one launch
 
     def step():
         prefill()
-        d_partial()
-        d_merge()
+        d_fused()
 
     for _ in range(args.warmup):
         step()
@@ -506,7 +507,7 @@ def main():
     K = args.steps
 
     # the timed region: K whole steps, an event between consecutive launches
-    evs = [_events(torch, 5) for _ in range(K)]
+    evs = [_events(torch, 4) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -516,25 +517,22 @@ def main():
         e[1].record()
         p_attn()
         e[2].record()
-        d_partial()
+        d_fused()
         e[3].record()
-        d_merge()
-        e[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = statistics.mean(e[0].elapsed_time(e[4]) for e in evs)
+    step_ms = statistics.mean(e[0].elapsed_time(e[3]) for e in evs)
 
     def launch_stats(a, b):
         return _stats([e[a].elapsed_time(e[b]) for e in evs])
-    st_pack, st_attn, st_part, st_merge = (launch_stats(i, i + 1) for i in range(4))
+    st_pack, st_attn, st_dec = (launch_stats(i, i + 1) for i in range(3))
     # per-launch medians over the K steps (robust to a host stall in one interval)
     pack_mean, attn_mean = st_pack["median_ms"], st_attn["median_ms"]
-    part_mean, merge_mean = st_part["median_ms"], st_merge["median_ms"]
     pre_mean = pack_mean + attn_mean
     flops = pcfg.flops()
     value = flops / (pre_mean * 1e-3) / 1e12
     attn_tflops = flops / (attn_mean * 1e-3) / 1e12
-    dec_us = (part_mean + merge_mean) * 1e3
+    dec_us = st_dec["median_ms"] * 1e3
     print(f"[bench] timed {K} steps: {step_ms * 1e3:.1f} us per step; prefill "
           f"{pre_mean * 1e3:.1f} us, decode {dec_us:.1f} us", file=sys.stderr, flush=True)
 
@@ -568,9 +566,8 @@ def main():
                     "frac_mfma_peak": round(value / MI355X_BF16_DENSE_TFLOPS, 4)},
         "decode_gqa_kv1641": {
             "split_len": dinfo["split_len"], "max_splits": dinfo["max_splits"],
-            "us_per_call": round(dec_us, 2),
-            "partial_us": round(part_mean * 1e3, 2),
-            "merge_us": round(merge_mean * 1e3, 2),
+            "us_per_call": round(dec_us, 2), "launches": 1,
+            "spread": st_dec["spread"],
             "alg_gbps": round(dinfo["alg_bytes"] / (dec_us * 1e-6) / 1e9, 1),
             "cache": "as left by the preceding prefill in the step"},
     }
@@ -581,18 +578,18 @@ def main():
         def flush():
             flush_buf.zero_()
 
-        # single-token decode: cold (flushed) and hot
+        # single-token decode: cold (flushed) and hot, in one launch and in two
+        fc = time_calls(torch, [d_fused], 20, flush=flush)
+        fh = time_calls(torch, [d_fused], 50)
+        line["decode_gqa_kv1641"]["cold_us"] = round(fc[0]["median_ms"] * 1e3, 2)
+        line["decode_gqa_kv1641"]["hot_us"] = round(fh[0]["median_ms"] * 1e3, 2)
         cold = time_calls(torch, [d_partial, d_merge], 20, flush=flush)
         hot = time_calls(torch, [d_partial, d_merge], 50)
-        hot_ms = hot[0]["median_ms"] + hot[1]["median_ms"]
-        line["decode_gqa_kv1641"]["cold_us"] = round(
-            (cold[0]["median_ms"] + cold[1]["median_ms"]) * 1e3, 2)
-        line["decode_gqa_kv1641"]["hot_us"] = round(hot_ms * 1e3, 2)
-        fc = time_calls(torch, [dinfo["fused"]], 20, flush=flush)
-        fh = time_calls(torch, [dinfo["fused"]], 50)
-        line["decode_gqa_kv1641"]["fused_single_launch"] = {
-            "cold_us": round(fc[0]["median_ms"] * 1e3, 2),
-            "hot_us": round(fh[0]["median_ms"] * 1e3, 2)}
+        line["decode_gqa_kv1641"]["two_launches"] = {
+            "cold_us": round((cold[0]["median_ms"] + cold[1]["median_ms"]) * 1e3, 2),
+            "hot_us": round((hot[0]["median_ms"] + hot[1]["median_ms"]) * 1e3, 2),
+            "partial_us_hot": round(hot[0]["median_ms"] * 1e3, 2),
+            "merge_us_hot": round(hot[1]["median_ms"] * 1e3, 2)}
         if args.split_sweep:
             sweep = {}
             for sl in (16, 32, 48, 64, 112, 208):

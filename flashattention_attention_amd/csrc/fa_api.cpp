@@ -124,7 +124,7 @@ fa::PrefillArgs prefill_args(const void* q, int64_t q_sb, int64_t q_ss, int64_t 
                              float* row_sum, int batch, int seqlen_q, int seqlen_kv,
                              int n_heads_q, int n_heads_kv, int causal, float softmax_scale,
                              const int32_t* kv_lens, int window, const float* sink_logits) {
-  fa::PrefillArgs a;
+  fa::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_sum = row_sum;
   a.q_sb = q_sb; a.q_ss = q_ss; a.q_sh = q_sh;
   a.k_sb = k_sb; a.k_ss = k_ss; a.k_sh = k_sh;

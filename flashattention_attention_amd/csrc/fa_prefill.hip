@@ -230,6 +230,17 @@ vt_pack_kernel(const unsigned short* __restrict__ v, int64_t v_sb, int64_t v_ss,
 // G/8 whole groups; G dividing 8 spreads each group over 8/G XCDs (the
 // group's blocks dealt out in longest-first order); any other G falls back
 // to a plain longest-first order.
+//
+// Serial order (G a multiple of 8, a group's blocks at least one XCD's worth
+// of work-group slots): each XCD takes its G/8 groups one after the other,
+// each group's blocks longest first. With every block of a group started
+// together, their K/V^T tile reads run in step, so the XCD's L2 serves one
+// group's tiles at a time instead of interleaving G/8 groups that do not fit
+// it together. The causal blocks of a group end at different times, so the
+// next group's blocks start one by one and all end together; that group
+// (every second one on an XCD) walks its tiles from the last to the first,
+// which puts its blocks in step again, reading the same tile at the same
+// time.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int wg_count(int groups, int per_group, int nqb) {
   const int m = per_group * nqb;                     // work-groups of one group
@@ -241,15 +252,34 @@ __host__ __device__ inline int wg_count(int groups, int per_group, int nqb) {
 struct WgItem {
   int b, hk, unit, qb;   // batch entry, KV head, unit of query heads in the group, query block
   bool valid;
+  bool rev;              // walk the key tiles from the last to the first
 };
+
+// Work-group slots per XCD at two work-groups per compute unit.
+constexpr int kWgSlotsPerXcd = 32 * 2;
+
+// Whether a launch uses the serial order (host side; the kernel reads it
+// from PrefillArgs::wg_serial).
+__host__ __device__ inline bool wg_serial_fits(int groups, int per_group, int nqb) {
+  return groups % 8 == 0 && groups > 8 && (int64_t)per_group * nqb >= kWgSlotsPerXcd;
+}
 
 // per_group: work units (sets of query heads) per group.
 __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int per_group,
-                                          int nqb) {
+                                          int nqb, bool serial = false) {
   const int groups = batch * n_heads_kv;
   int g, u, rank;                                    // rank 0 = longest block
-  bool valid = true;
-  if (groups % 8 == 0) {
+  bool valid = true, rev = false;
+  if (serial && groups % 8 == 0) {
+    const int x = id & 7, j = id >> 3;
+    const int per_g = per_group * nqb;
+    const int gi = j / per_g;                        // this XCD's gi-th group
+    const int r = j - gi * per_g;
+    rank = r / per_group;
+    u = r % per_group;
+    g = gi * 8 + x;
+    rev = (gi & 1) != 0;
+  } else if (groups % 8 == 0) {
     const int x = id & 7, j = id >> 3;
     const int per_level = (groups >> 3) * per_group;
     rank = j / per_level;
@@ -276,6 +306,7 @@ __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int
   w.unit = u;
   w.qb = nqb - 1 - rank;
   w.valid = valid;
+  w.rev = rev;
   return w;
 }
 
@@ -341,7 +372,8 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   const int per_group = a.n_heads_q / a.n_heads_kv;
   int nunits = nqb;
   if constexpr (SPLIT) nunits = sp.n_units;
-  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nunits);
+  const WgItem item =
+      wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nunits, a.wg_serial != 0);
   if (!item.valid) return;
   int qb = item.qb, half = -1;   // half: -1 whole block, else which half of its key tiles
   if constexpr (SPLIT) {
@@ -398,6 +430,12 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   }
   const int ntiles_all = (a.seqlen_kv + BN - 1) / BN;
   const int wave_first_qpos = q0 + qw * 32 + off;
+  // Absolute index of the t-th tile the loop visits (the serial order walks
+  // every second group's tiles backwards; the online softmax takes the tiles
+  // in any order).
+  const int tstep = item.rev ? -1 : 1;
+  const int tfirst = item.rev ? tb + ntiles - 1 : tb;
+  auto tile = [&](int t) { return tfirst + tstep * t; };
 
   const unsigned short* kp =
       (const unsigned short*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
@@ -407,7 +445,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
 
   const unsigned lds_base = (unsigned)(uintptr_t)(lptr_t)lds;
 
-  // DMA of this wave's share of the K rows / V^T bytes of tile tb + t to LDS
+  // DMA of this wave's share of the K rows / V^T bytes of tile tile(t) to LDS
   // offset dst. DMA instruction j of a wave writes rows R0 .. R0 + RPI - 1 of
   // the tile (R0 = (wave * K_INSTR + j) * RPI, wave-uniform); lane l takes row
   // R0 + l / CPR, logical chunk (l % CPR) ^ (row & SWZ). R0 is a multiple of
@@ -418,7 +456,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   // ragged last tile clamps each lane's row instead (rows past the end repeat
   // the last row; the mask zeroes them).
   auto issue_k = [&](int t, unsigned dst) {
-    const int t0 = (tb + t) * BN;
+    const int t0 = tile(t) * BN;
     unsigned ln = (unsigned)lane;
     asm volatile("" : "+v"(ln));
     const unsigned lrow = ln / CPR;
@@ -449,7 +487,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       // transpose read touches over distinct banks. The swizzle depends on the
       // row only through its offset inside the instruction, so the lane part of
       // the address is the same for every instruction of the tile.
-      const int t0 = (tb + t) * BN;
+      const int t0 = tile(t) * BN;
       unsigned ln = (unsigned)lane;
       asm volatile("" : "+v"(ln));
       const unsigned lrow = ln / CPR;
@@ -473,7 +511,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       }
       return;
     }
-    const char* base = vtp + (int64_t)(tb + t) * VT;
+    const char* base = vtp + (int64_t)tile(t) * VT;
     unsigned ln = (unsigned)lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -643,7 +681,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
     __syncthreads();   // K(0) is read everywhere before K(2) overwrites it
     float tm = 0.0f;   // row max of the next tile to exponentiate (log2 units)
     if (ntiles > 0) {
-      if (needs_mask(tb * BN)) apply_mask(sa, tb * BN);
+      if (needs_mask(tile(0) * BN)) apply_mask(sa, tile(0) * BN);
       tm = row_max(sa);
     }
 
@@ -674,7 +712,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       // P.V of tile t with the row max of tile t+1 interleaved (its base moves
       // at the top of the next step, after this P.V, as before); a straddling
       // tile t+1 is masked first. After the last tile the max is unused.
-      if (t + 1 < ntiles && needs_mask((tb + t + 1) * BN)) apply_mask(nxt, (tb + t + 1) * BN);
+      if (t + 1 < ntiles && needs_mask(tile(t + 1) * BN)) apply_mask(nxt, tile(t + 1) * BN);
       pv(lds + VST[P], pk);
       tm = row_max(nxt);
       {
@@ -717,7 +755,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
           if (i + AHEAD < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
       }
-      const float base = prep(sc, (tb + t) * BN);
+      const float base = prep(sc, tile(t) * BN);
       u32x4 pk[NKS];
       expo(sc, base, pk);
       pv(lds + ST_[ST] + KT, pk);
@@ -1158,10 +1196,14 @@ hipError_t launch_pack_d(const PrefillArgs& a, const VtArgs& w, hipStream_t stre
 }
 
 template <int D, bool BF16>
-hipError_t launch_attn_d(const PrefillArgs& a, const VtArgs& w, bool unnorm, hipStream_t stream) {
+hipError_t launch_attn_d(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hipStream_t stream) {
   constexpr int BM = block_rows(D);
-  const int per_group = a.n_heads_q / a.n_heads_kv;
-  const int nqb = (a.seqlen_q + BM - 1) / BM;
+  const int per_group = a0.n_heads_q / a0.n_heads_kv;
+  const int nqb = (a0.seqlen_q + BM - 1) / BM;
+  PrefillArgs a = a0;
+  // head_dim 256: one group's K/V^T (2 x 512 bytes per key) outgrows an XCD's
+  // L2 at a few thousand keys, so its groups run one at a time per XCD.
+  a.wg_serial = D == 256 && wg_serial_fits(a.batch * a.n_heads_kv, per_group, nqb) ? 1 : 0;
   const auto go = [&](auto hp_c) {
     constexpr int HP = decltype(hp_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
