@@ -36,7 +36,7 @@ struct PrefillArgs {
   const int32_t* kv_lens;  // device [batch] valid KV length per sequence, or null
   int window;              // > 0: key j visible only if j > q_pos - window
   const float* sink_logits;  // device [n_heads_q] per-head sink logit, or null
-  int wg_serial;           // work-group order: 1 = one group at a time per XCD (set by the launcher)
+  int wg_serial;           // serial work-group order: work-group slots per XCD (0 = off; set by the launcher)
 };
 
 struct DecodeArgs {

@@ -231,16 +231,16 @@ vt_pack_kernel(const unsigned short* __restrict__ v, int64_t v_sb, int64_t v_ss,
 // group's blocks dealt out in longest-first order); any other G falls back
 // to a plain longest-first order.
 //
-// Serial order (G a multiple of 8, a group's blocks at least one XCD's worth
-// of work-group slots): each XCD takes its G/8 groups one after the other,
-// each group's blocks longest first. With every block of a group started
-// together, their K/V^T tile reads run in step, so the XCD's L2 serves one
-// group's tiles at a time instead of interleaving G/8 groups that do not fit
-// it together. The causal blocks of a group end at different times, so the
-// next group's blocks start one by one and all end together; that group
-// (every second one on an XCD) walks its tiles from the last to the first,
-// which puts its blocks in step again, reading the same tile at the same
-// time.
+// Serial order (with S work-group slots per XCD): for G a multiple of 8 and
+// a group's blocks at least S, each XCD takes its G/8 groups one after the
+// other, each group's blocks longest first; for G dividing 8 the order above
+// already runs one group per XCD. Work-groups started together read their
+// K/V^T tiles in step, so the XCD's L2 serves one group's tiles at a time
+// instead of interleaving groups that do not fit it together. The causal
+// blocks of a round of S work-groups end at different times, so the next
+// round starts one by one and (longest first) all of it ends together: every
+// second round on an XCD walks its tiles from the last to the first, which
+// puts its blocks in step again, reading the same tile at the same time.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int wg_count(int groups, int per_group, int nqb) {
   const int m = per_group * nqb;                     // work-groups of one group
@@ -255,22 +255,25 @@ struct WgItem {
   bool rev;              // walk the key tiles from the last to the first
 };
 
-// Work-group slots per XCD at two work-groups per compute unit.
-constexpr int kWgSlotsPerXcd = 32 * 2;
-
-// Whether a launch uses the serial order (host side; the kernel reads it
-// from PrefillArgs::wg_serial).
-__host__ __device__ inline bool wg_serial_fits(int groups, int per_group, int nqb) {
-  return groups % 8 == 0 && groups > 8 && (int64_t)per_group * nqb >= kWgSlotsPerXcd;
+// Whether a launch with `slots` work-group slots per XCD uses the serial
+// order: more work-groups per XCD than one round of slots, and for G a
+// multiple of 8 at least a round per group (host side; the kernel reads the
+// slot count from PrefillArgs::wg_serial).
+__host__ __device__ inline bool wg_serial_fits(int groups, int per_group, int nqb, int slots) {
+  const int64_t per_g = (int64_t)per_group * nqb;
+  if (groups % 8 == 0) return groups > 8 && per_g >= slots;
+  if (8 % groups == 0) return per_g * groups / 8 > slots;
+  return false;
 }
 
-// per_group: work units (sets of query heads) per group.
+// per_group: work units (sets of query heads) per group. serial_slots > 0:
+// the serial order for that many work-group slots per XCD.
 __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int per_group,
-                                          int nqb, bool serial = false) {
+                                          int nqb, int serial_slots = 0) {
   const int groups = batch * n_heads_kv;
   int g, u, rank;                                    // rank 0 = longest block
   bool valid = true, rev = false;
-  if (serial && groups % 8 == 0) {
+  if (serial_slots > 0 && groups % 8 == 0) {
     const int x = id & 7, j = id >> 3;
     const int per_g = per_group * nqb;
     const int gi = j / per_g;                        // this XCD's gi-th group
@@ -278,7 +281,7 @@ __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int
     rank = r / per_group;
     u = r % per_group;
     g = gi * 8 + x;
-    rev = (gi & 1) != 0;
+    rev = ((j / serial_slots) & 1) != 0;
   } else if (groups % 8 == 0) {
     const int x = id & 7, j = id >> 3;
     const int per_level = (groups >> 3) * per_group;
@@ -293,6 +296,7 @@ __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int
     valid = i < per_group * nqb;
     rank = i / per_group;
     u = i % per_group;
+    rev = serial_slots > 0 && ((j / serial_slots) & 1) != 0;
   } else {
     const int per_level = groups * per_group;
     rank = id / per_level;
@@ -372,8 +376,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   const int per_group = a.n_heads_q / a.n_heads_kv;
   int nunits = nqb;
   if constexpr (SPLIT) nunits = sp.n_units;
-  const WgItem item =
-      wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nunits, a.wg_serial != 0);
+  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nunits, a.wg_serial);
   if (!item.valid) return;
   int qb = item.qb, half = -1;   // half: -1 whole block, else which half of its key tiles
   if constexpr (SPLIT) {
@@ -958,7 +961,7 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   const int dh = wave / QG;                  // which half of the head dims
   const int nqb = (a.seqlen_q + kBM - 1) / kBM;
   const int per_group = a.n_heads_q / a.n_heads_kv;
-  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group, nqb);
+  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group, nqb, a.wg_serial);
   if (!item.valid) return;
   const int qb = item.qb, b = item.b, hk = item.hk;
   const int h = hk * per_group + item.unit;
@@ -991,17 +994,22 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   const int ntiles = kv_end > kv_lo ? (kv_end + BN - 1) / BN - tb : 0;
   const int ntiles_all = (a.seqlen_kv + BN - 1) / BN;
   const int wave_first_qpos = q0 + qw * 32 + off;
+  // Absolute index of the t-th tile visited (backwards in every second round
+  // of the serial order).
+  const int tstep = item.rev ? -1 : 1;
+  const int tfirst = item.rev ? tb + ntiles - 1 : tb;
+  auto tile = [&](int t) { return tfirst + tstep * t; };
 
   const unsigned short* kp =
       (const unsigned short*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
   const char* vtp = (const char*)vt_ws + ((int64_t)b * a.n_heads_kv + hk) * ntiles_all * VT;
   const unsigned lds_base = (unsigned)(uintptr_t)(lptr_t)lds;
 
-  // DMA of tile tb + t into the stage at LDS offset st. K: one 1 KB row per
+  // DMA of tile tile(t) into the stage at LDS offset st. K: one 1 KB row per
   // instruction; lane p stores the row's 16-byte chunk p ^ (row & 15) at
   // position p (the swizzle that spreads an operand load over the banks).
   auto issue = [&](int t, unsigned st) {
-    const int t0 = (tb + t) * BN;
+    const int t0 = tile(t) * BN;
     // Recomputed per tile (one XOR each) rather than held across the loop:
     // the loop has no registers to spare for four offsets.
     unsigned lane16 = (unsigned)lane << 4;
@@ -1016,7 +1024,7 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
 #pragma unroll
     for (int j = 0; j < V_INSTR; ++j) {
       const int J = wave * V_INSTR + j;
-      dma16_at(vtp + (int64_t)(tb + t) * VT + J * 1024, (unsigned)lane << 4,
+      dma16_at(vtp + (int64_t)tile(t) * VT + J * 1024, (unsigned)lane << 4,
                lds_base + st + KT + J * 1024);
     }
   };
@@ -1130,7 +1138,7 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * c + e] += p[e];
     }
-    const float base = prep(s, (tb + t) * BN);
+    const float base = prep(s, tile(t) * BN);
     u32x4 pk[NKS];
     expo(s, base, pk);
     pv(lds + ST_[ST] + KT, pk);
@@ -1203,7 +1211,8 @@ hipError_t launch_attn_d(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hi
   PrefillArgs a = a0;
   // head_dim 256: one group's K/V^T (2 x 512 bytes per key) outgrows an XCD's
   // L2 at a few thousand keys, so its groups run one at a time per XCD.
-  a.wg_serial = D == 256 && wg_serial_fits(a.batch * a.n_heads_kv, per_group, nqb) ? 1 : 0;
+  constexpr int kSlots = 32 * 2;   // two work-groups per compute unit
+  a.wg_serial = D == 256 && wg_serial_fits(a.batch * a.n_heads_kv, per_group, nqb, kSlots) ? kSlots : 0;
   const auto go = [&](auto hp_c) {
     constexpr int HP = decltype(hp_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
@@ -1270,9 +1279,14 @@ hipError_t launch_split_d(const PrefillArgs& a, const VtArgs& w, const SplitPlan
 }
 
 template <bool BF16>
-hipError_t launch_attn_512(const PrefillArgs& a, const VtArgs& w, bool unnorm, hipStream_t stream) {
-  const int per_group = a.n_heads_q / a.n_heads_kv;
-  const int nqb = (a.seqlen_q + 127) / 128;
+hipError_t launch_attn_512(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hipStream_t stream) {
+  const int per_group = a0.n_heads_q / a0.n_heads_kv;
+  const int nqb = (a0.seqlen_q + 127) / 128;
+  PrefillArgs a = a0;
+  // One work-group per compute unit; the K/V^T of a group (2 x 1 KB per key)
+  // outgrows an XCD's L2 at a few thousand keys.
+  constexpr int kSlots = 32;
+  a.wg_serial = wg_serial_fits(a.batch * a.n_heads_kv, per_group, nqb, kSlots) ? kSlots : 0;
   const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group, nqb));
   if (unnorm)
     hipLaunchKernelGGL((prefill512_kernel<BF16, true>), grid, dim3(512), 0, stream, a,

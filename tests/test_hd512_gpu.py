@@ -139,7 +139,9 @@ def test_hd512_packed_matches_fused(torch_gpu):
 
 def test_hd512_full_size(torch_gpu):
     """The 4096-token multi-query workload at head_dim 512, in the configuration
-    the benchmark times: sampled rows against the oracle, repeat identity."""
+    the benchmark times: sampled rows against the oracle (one inside every
+    128-row block, so every work-group of the serial order, half of which
+    walk their key tiles backwards, is checked), repeat identity."""
     cfg = inputs.HD512_PREFILL
     _say(cfg.name)
     x = inputs.make_prefill_inputs(cfg)
@@ -150,7 +152,8 @@ def test_hd512_full_size(torch_gpu):
     rng = np.random.default_rng(cfg.seed)
     S = cfg.seqlen_q
     rows = sorted({0, 1, 31, 32, 127, 128, 129, S // 2, S - 129, S - 128, S - 2, S - 1}
-                  | set(rng.integers(0, S, 6).tolist()))
+                  | set(rng.integers(0, S, 6).tolist())
+                  | {qb * 128 + 61 for qb in range(-(-S // 128))})
     ref = oracle.prefill(x["q"], x["k"], x["v"], scale=cfg.scale, causal=True, dtype=cfg.dtype,
                          rows=rows)
     o, lse, rs = runs[0]
