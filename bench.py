@@ -443,7 +443,8 @@ def run_profiling_aid(torch, fa, inputs, args):
                               lse=tens["lse"], prepare=True)
         fns, label = [pack, attn, merge], cfg.name + "_sink"
     else:
-        cfg = inputs.GQA_DECODE if args.only == "decode" else inputs.LONG_DECODE
+        cfg = {"decode": inputs.GQA_DECODE, "long_decode": inputs.LONG_DECODE,
+               "long_decode_h28kv4": inputs.LONG_DECODE_G7}[args.only]
         part, merge, info = decode_setup(torch, fa, cfg)
         fns, label = [part, merge, info["fused"]], cfg.name
     for _ in range(args.warmup):
@@ -466,7 +467,7 @@ def main():
                     help="also time the single-token decode at several split lengths")
     ap.add_argument("--only", choices=["prefill", "decode", "long_decode", "large_head",
                                               "window", "hd512", "sink", "few_heads_split",
-                                              "prefill_f16"],
+                                              "prefill_f16", "long_decode_h28kv4"],
                     help="profiling aid: run only this component (warmup + steps) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="profiling aid: time a plain device-to-device copy of this many "
