@@ -148,15 +148,17 @@ def prefill_direct_setup(torch, fa, cfg):
                       prepare=True)
 
 
-def prefill_kernel_name(cfg, split=False):
-    """The attention kernel's template name as rocprofv3 reports it."""
+def prefill_kernel_name(cfg, split=False, vrow=False):
+    """The attention kernel's template name as rocprofv3 reports it (vrow: the
+    one-launch fp16 form that reads V's rows)."""
     if cfg.head_dim == 512:
         return (f"prefill512_kernel<{str(cfg.dtype == 'bf16').lower()}, "
                 f"{str(cfg.out_unnormalized).lower()}>")
     group = cfg.n_heads_q // cfg.n_heads_kv
     hp = 2 if cfg.head_dim <= 128 and group % 2 == 0 else 1
     return (f"prefill_kernel<{cfg.head_dim}, {str(cfg.dtype == 'bf16').lower()}, "
-            f"{str(cfg.out_unnormalized).lower()}, {hp}, {str(split).lower()}>")
+            f"{str(cfg.out_unnormalized).lower()}, {hp}, {str(split).lower()}, "
+            f"{str(vrow).lower()}>")
 
 
 def decode_kernel_name(cfg):
@@ -651,6 +653,15 @@ def main():
         rg = time_calls(torch, [g_partial, g_merge], 20, flush=flush)
         rgf = time_calls(torch, [ginfo["fused"]], 20, flush=flush)
         g_ms = rg[0]["median_ms"] + rg[1]["median_ms"]
+        g_gbps = ginfo["kv_bytes"] / (rg[0]["median_ms"] * 1e-3) / 1e9
+        gk = decode_kernel_name(gcfg)
+        rooflines["decode_partial_batched_long_h28kv4"] = {
+            "bound": "hbm", "achieved": round(g_gbps, 1), "peak": MI355X_HBM_GBPS,
+            "unit": "GB/s", "frac": round(g_gbps / MI355X_HBM_GBPS, 4),
+            "traffic": measured_traffic(gk, gcfg.name, "fa_decode.hip"), "kernel": gk,
+            "us_per_launch": round(rg[0]["median_ms"] * 1e3, 1),
+            "per_launch": f"{ginfo['kv_bytes'] / 1e9:.4f} GB of K+V (each cached key and value "
+                          f"row read once)"}
         line["decode_batched_long_h28kv4"] = {
             "workload": gcfg.name, "split_len": ginfo["split_len"],
             "max_splits": ginfo["max_splits"], "kv_gb": round(ginfo["kv_bytes"] / 1e9, 4),
@@ -706,6 +717,13 @@ def main():
                                    "us_per_call": round(r[0]["median_ms"] * 1e3, 1),
                                    "spread": r[0]["spread"], "tflops": round(gt, 2),
                                    "frac_mfma_peak": round(gt / MI355X_BF16_DENSE_TFLOPS, 4)}
+        vk = prefill_kernel_name(gcfg, vrow=True)
+        rooflines["prefill_gqa_s3314_f16_one_launch"] = {
+            "bound": "mfma", "achieved": round(gt, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(gt / MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": measured_traffic(vk, gcfg.name, "fa_prefill.hip"), "kernel": vk,
+            "us_per_launch": round(r[0]["median_ms"] * 1e3, 2),
+            "per_launch": f"{gcfg.flops() / 1e9:.2f} GFLOP (fp16 peak = bf16 peak)"}
         del g_call
         print("[bench] large-head prefill", file=sys.stderr, flush=True)
 
