@@ -34,6 +34,7 @@
 // deterministic for a given split plan.
 #include "fa_internal.h"
 
+#include <climits>
 #include <mutex>
 
 // Scratch of the single-launch decode for callers that cannot allocate
@@ -697,6 +698,36 @@ __device__ __forceinline__ void split_run(const DecodeArgs& a, int b, int h0, in
     split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
 }
 
+// Launch order of the decode work-groups. A "cluster" is the work-groups that
+// read the same K/V rows: one sequence, one KV head, one split (or group of
+// splits), and the q_per_kv head groups of that KV head. Work-group i runs on
+// XCD i % 8, which has its own L2: a cluster's work-groups all go to one XCD,
+// so after the first fetch its rows come from that L2 (the loads are
+// non-temporal but reach L2), and consecutive clusters, KV heads fastest
+// (the same token rows), go to consecutive XCDs. With one head group per KV
+// head this is the plain (KV head, split, sequence) order.
+struct DecItem {
+  int b, hg, y;   // sequence, head group, split (or split group)
+  bool valid;
+};
+__host__ __device__ inline int64_t dec_grid(int batch, int n_heads_kv, int q_per_kv, int ny) {
+  const int64_t c = (int64_t)batch * n_heads_kv * ny;
+  return 8 * ((c + 7) / 8) * q_per_kv;
+}
+__device__ inline DecItem dec_item(int id, int batch, int n_heads_kv, int q_per_kv, int ny) {
+  const int x = id & 7, m = id >> 3;
+  const int j = m % q_per_kv;
+  const int64_t c = (int64_t)(m / q_per_kv) * 8 + x;
+  DecItem it;
+  it.valid = c < (int64_t)batch * n_heads_kv * ny;
+  const int hk = (int)(c % n_heads_kv);
+  const int64_t r = c / n_heads_kv;
+  it.y = (int)(r % ny);
+  it.b = (int)(r / ny);
+  it.hg = hk * q_per_kv + j;
+  return it;
+}
+
 // One wave per (sequence, group of G query heads, split): the split's
 // normalized partial output and its natural-log LSE.
 template <int D, int G, bool BF16>
@@ -705,9 +736,10 @@ decode_partial_kernel(DecodeArgs a) {
   constexpr int LPK = lanes_per_row(D);
   constexpr int EPL = D / LPK;
   const int lane = threadIdx.x;
-  const int h0 = blockIdx.x * G;   // head groups fastest: the waves reading the
-  const int s = blockIdx.y;        // same tokens' rows are dispatched together
-  const int b = blockIdx.z;
+  const int qpk = a.n_heads_q / a.n_heads_kv / G;   // head groups per KV head
+  const DecItem it = dec_item(blockIdx.x, a.batch, a.n_heads_kv, qpk, a.max_splits);
+  if (!it.valid) return;
+  const int h0 = it.hg * G, s = it.y, b = it.b;
   const int L = a.kv_lens[b];
   const int lo = s * a.split_len;
   if (L < 1 || lo >= L) return;          // empty split: nothing read or written
@@ -833,7 +865,10 @@ decode_fused_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(256))) float pbuf[NW][decode_lds_floats(D, G, BF16)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hg = blockIdx.x, h0 = hg * G, y = blockIdx.y, b = blockIdx.z;
+  const int qpk = a.n_heads_q / a.n_heads_kv / G;   // head groups per KV head
+  const DecItem it = dec_item(blockIdx.x, a.batch, a.n_heads_kv, qpk, a.max_wg);
+  if (!it.valid) return;
+  const int hg = it.hg, h0 = hg * G, y = it.y, b = it.b;
   const int L = a.kv_lens[b];
   const int ns = L < 1 ? 0 : (L + a.split_len - 1) / a.split_len;
   const bool bad = ns < 1 || ns > a.max_splits;
@@ -903,12 +938,12 @@ decode_fused_kernel(DecodeArgs a) {
   // last one merge. The partial went out as agent-scope stores, so waiting for
   // their completion publishes it; an agent-scope release fence would instead
   // write back the whole L2 of this XCD from every work-group.
-  int* counter = a.counters + (int64_t)b * gridDim.x + hg;
+  int* counter = a.counters + (int64_t)b * (a.n_heads_q / G) + hg;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)
     is_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (int)gridDim.y - 1;
+              a.max_wg - 1;
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // drop stale cached partials
@@ -1031,7 +1066,9 @@ decode_fused_kernel(DecodeArgs a) {
 
 template <int D, bool BF16>
 hipError_t launch_partial_d(const DecodeArgs& a, int g, hipStream_t stream) {
-  const dim3 grid(a.n_heads_q / g, a.max_splits, a.batch);
+  const int64_t n = dec_grid(a.batch, a.n_heads_kv, a.n_heads_q / a.n_heads_kv / g, a.max_splits);
+  if (n > INT_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n);
   switch (g) {
 #define FA_CASE(G) \
   case G: hipLaunchKernelGGL((decode_partial_kernel<D, G, BF16>), grid, dim3(64), 0, stream, a); break;
@@ -1045,7 +1082,9 @@ hipError_t launch_partial_d(const DecodeArgs& a, int g, hipStream_t stream) {
 
 template <int D, bool BF16, int NW>
 hipError_t launch_fused_dw(const DecodeArgs& a, int g, hipStream_t stream) {
-  const dim3 grid(a.n_heads_q / g, a.max_wg, a.batch);
+  const int64_t n = dec_grid(a.batch, a.n_heads_kv, a.n_heads_q / a.n_heads_kv / g, a.max_wg);
+  if (n > INT_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n);
   switch (g) {
 #define FA_CASE(G)                                                                           \
   case G:                                                                                    \
