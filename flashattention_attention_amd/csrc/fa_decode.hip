@@ -775,6 +775,41 @@ __device__ __forceinline__ void merge_head(const float* pl, const float* po_row0
   constexpr int EPL = D / 64;
   constexpr int U = 32;                    // partials in flight per step
   const float* po = po_row0 + lane * EPL;
+  if (ns <= U) {
+    // Common case: the LSEs and every partial row are requested together (one
+    // memory round trip); same arithmetic, in the same order, as below.
+    const float lv = pl[min(lane, ns - 1)];
+    float v[U][EPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sj = min(u, ns - 1);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[u][e] = po[(int64_t)sj * D + e];
+    }
+    float M = lane < ns ? lv : -INFINITY;
+#pragma unroll
+    for (int x = 1; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
+    const float wl = lane < ns ? __expf(lv - M) : 0.0f;
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < ns) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(w, v[u][e], acc[e]);
+      }
+    }
+    float wsum = wl;
+#pragma unroll
+    for (int x = 1; x < 64; x *= 2) wsum += __shfl_xor(wsum, x);
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[lane * EPL + e] = acc[e] * inv;
+    if (lane == 0) *lse_out = M + __logf(wsum);
+    return;
+  }
   float M = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += 64)
     if (s0 + lane < ns) M = fmaxf(M, pl[s0 + lane]);
