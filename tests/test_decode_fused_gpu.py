@@ -113,6 +113,7 @@ def test_fused_gqa_decode_workload(torch_gpu, split_len):
     ("f16", 128, 28, 4, 48, 3), ("bf16", 128, 32, 8, 16, 20), ("f16", 64, 8, 8, 32, 0),
     ("bf16", 256, 16, 2, 48, 5), ("f16", 128, 12, 1, 112, 1), ("bf16", 64, 6, 2, 16, 9),
     ("f16", 256, 4, 4, 16, 0),
+    ("f16", 128, 32, 4, 48, 0),     # 4 heads per wave, 4-wave work-groups, P.V on MFMA
 ])
 def test_fused_lengths_and_spare_splits(torch_gpu, dtype, D, hq, hkv, split_len, extra):
     """KV lengths {1, 29, 52, 512, 1641} in one batch, with `extra` spare splits
