@@ -22,12 +22,10 @@
 //    reduced with DPP row permutes, and the online-softmax update is done
 //    once per block and head (section 3.2 of the same page gives the per-row
 //    form: new max, correction factor, exponential, running sum and output);
-//  * with several query heads per wave (head_dim <= 128) the per-head work
-//    outweighs the loads and moves to the matrix cores: for fp16 caches from
-//    4 heads per wave both Q.K^T and P.V (split_attend_mfma_pv), for bf16
-//    from 5 heads Q.K^T only (split_attend_mfma); each K row then serves up
-//    to 16 heads in one 16x16x32 MFMA, and the exponentials are spread one
-//    per (key, head).
+//  * from 4 query heads per wave (head_dim <= 128) the per-head work
+//    outweighs the loads and moves to the matrix cores: Q.K^T and P.V
+//    (split_attend_mfma_pv); each K row then serves up to 16 heads in one
+//    16x16x32 MFMA, and the exponentials are spread one per (key, head).
 //
 // Each split emits a normalized partial O_s and its natural-log LSE_s. The
 // merge then combines the partials by LSE in a fixed order, so the result is
@@ -251,21 +249,7 @@ __device__ __forceinline__ void split_attend(const DecodeArgs& a, int b, int h0,
   }
 }
 
-// The same split with Q.K^T on the matrix cores, for waves that serve several
-// query heads (D <= 128). Per 32-key block:
-//  * S^T (16 keys x 16 heads per MFMA, v_mfma_f32_16x16x32) = K . Q^T: lane l
-//    loads K row l % 16 of a 16-key half, dims kk*32 + (l/16)*8 .. +7 (16
-//    contiguous bytes), and holds Q of head l % 16 for the same dims (zero for
-//    heads past G); it receives S for keys 4*(l/16) .. +3 of head l % 16;
-//  * the block max and the exponentials run in that layout: one exponential
-//    per (key, head) pair, wherever G is;
-//  * P (fp32) goes through a per-wave LDS buffer to the row layout of
-//    split_attend, whose P.V (fp32 FMAs on the half V elements) and final row-
-//    slot sums are unchanged.
-// pw: this wave's LDS scratch, kPRows * kPStride floats.
-constexpr int kPRows = 32;      // keys per block
-constexpr int kPStride = 20;    // floats per key row: 16 heads + 4 pad (no bank conflicts)
-
+// 16x16x32 MFMA on packed halves (A, B: 8 halves per lane; C: 4 floats per lane).
 template <bool BF16>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   if constexpr (BF16)
@@ -276,182 +260,19 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Q.K^T on the matrix cores from 5 heads per wave: there the VALU form is
-// bound by its per-head dot products and exponentials (at 32 cached keys per
-// block, 4 KV heads and 28 or 32 query heads this form was 1.3-1.4x faster);
-// at 3 and 4 heads both reached the same HBM rate. fp16 caches take the form
-// with P.V on the matrix cores as well (decode_pv_on_mfma), from 4 heads.
-__host__ __device__ constexpr bool decode_uses_mfma(int d, int g) { return d <= 128 && g >= 5; }
-
-template <int D, int G, bool BF16>
-__device__ __forceinline__ void split_attend_mfma(const DecodeArgs& a, int b, int h0, int lo,
-                                                  int hi, int lane, float* pw, float (&m)[G],
-                                                  float (&l)[G],
-                                                  float (&o)[G][D / lanes_per_row(D)]) {
-  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  static_assert(G >= 1 && G <= 16, "at most 16 heads per wave");
-  constexpr int LPK = lanes_per_row(D);    // lanes per V row (row layout)
-  constexpr int EPL = D / LPK;
-  constexpr int W = EPL / 8;
-  constexpr int KPS = 64 / LPK;            // V rows per load step
-  constexpr int BK = kPRows;               // keys per block
-  constexpr int NB = BK / KPS;             // V load steps per block
-  constexpr int NKK = D / 32;              // MFMA k-steps
-  constexpr int NPV = (G + 3) / 4;         // 16-byte reads of one key's P row
-
-  const int hk = h0 / (a.n_heads_q / a.n_heads_kv);
-  const int slot = lane / LPK;
-  const int c = lane % LPK;
-  const int n = lane & 15;                 // MFMA column: query head h0 + n
-  const int quad = lane >> 4;              // MFMA lane group
-
-  u32x4 qop[NKK];
-  {
-    const unsigned short* qp = (const unsigned short*)a.q + (int64_t)b * a.q_sb +
-                               (int64_t)(h0 + min(n, G - 1)) * a.q_sh + quad * 8;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      qop[kk] = n < G ? *(const u32x4*)(qp + kk * 32) : u32x4{0, 0, 0, 0};
-  }
-
-  const int64_t row0 = a.kv_offsets[b];
-  const unsigned short* kq =
-      (const unsigned short*)a.k + row0 * a.kv_st + (int64_t)hk * a.kv_sh + quad * 8;
-  const unsigned short* vbase =
-      (const unsigned short*)a.v + row0 * a.kv_st + (int64_t)hk * a.kv_sh + c * EPL;
-
-  // One block: K in the MFMA layout (two 16-key halves), V in the row layout.
-  // Rows past hi repeat row hi-1 (valid memory); their scores are masked.
-  auto load_block = [&](int start, u32x4 (&kd)[2][NKK], u32x4 (&vd)[NB][W]) {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int64_t key = min(start + sb * 16 + n, hi - 1);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        kd[sb][kk] = __builtin_nontemporal_load((const u32x4*)(kq + key * a.kv_st + kk * 32));
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int64_t key = min(start + j * KPS + slot, hi - 1);
-#pragma unroll
-      for (int w = 0; w < W; ++w)
-        vd[j][w] = __builtin_nontemporal_load((const u32x4*)(vbase + key * a.kv_st + w * 8));
-    }
-  };
-
-  float mc = -1e30f;   // running max (log2 units) of head column n
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
-  }
-
-  auto compute_block = [&](int start, const u32x4 (&kd)[2][NKK], const u32x4 (&vd)[NB][W]) {
-    f32x4 s[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      s[sb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[sb] = mfma16<BF16>(kd[sb][kk], qop[kk], s[sb]);
-    }
-    if (start + BK > hi) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (start + sb * 16 + quad * 4 + i >= hi) s[sb][i] = -INFINITY;
-    }
-    // Block max of head column n: in-lane over 8 keys, then over the 4 lane groups.
-    float lm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    lm = fmaxf(lm, __shfl_xor(lm, 16));
-    lm = fmaxf(lm, __shfl_xor(lm, 32));
-    const float bm = lm * a.scale_log2;    // the max commutes with the positive scale
-    const bool grow = bm > mc + kSlack;
-    if (__ballot(grow)) {
-      const float nm = grow ? bm : mc;
-      const float corr = __builtin_amdgcn_exp2f(mc - nm);
-      mc = nm;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float cg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), g));
-        l[g] *= cg;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[g][e] *= cg;
-      }
-    }
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pw[(sb * 16 + quad * 4 + i) * kPStride + n] =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], a.scale_log2, -mc));
-    // Other lanes' P values are read below: the writes must have landed.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const float* pr = pw + (j * KPS + slot) * kPStride;
-      float p[4 * NPV];
-#pragma unroll
-      for (int r = 0; r < NPV; ++r) {
-        const f32x4 v4 = *(const f32x4*)(pr + 4 * r);
-        p[4 * r] = v4[0];
-        p[4 * r + 1] = v4[1];
-        p[4 * r + 2] = v4[2];
-        p[4 * r + 3] = v4[3];
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        l[g] += p[g];
-#pragma unroll
-        for (int w = 0; w < W; ++w)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[g][w * 8 + 2 * e] = __builtin_fmaf(p[g], half_lo<BF16>(vd[j][w][e]),
-                                                 o[g][w * 8 + 2 * e]);
-            o[g][w * 8 + 2 * e + 1] = __builtin_fmaf(p[g], half_hi<BF16>(vd[j][w][e]),
-                                                     o[g][w * 8 + 2 * e + 1]);
-          }
-      }
-    }
-    // The next block's P writes must not overtake these reads.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  };
-
-  u32x4 ka[2][NKK], kb[2][NKK], va[NB][W], vb[NB][W];
-  load_block(lo, ka, va);
-  for (int start = lo; start < hi; start += 2 * BK) {
-    if (start + BK < hi) load_block(start + BK, kb, vb);
-    compute_block(start, ka, va);
-    if (start + BK >= hi) break;
-    if (start + 2 * BK < hi) load_block(start + 2 * BK, ka, va);
-    compute_block(start + BK, kb, vb);
-  }
-
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mc), g));
-#pragma unroll
-    for (int x = LPK; x < 64; x *= 2) {
-      l[g] += __shfl_xor(l[g], x);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[g][e] += __shfl_xor(o[g][e], x);
-    }
-  }
-}
-
-// The same split with P.V on the matrix cores as well (fp16 caches, D <= 128).
-// Per 32-key block:
+// The same split on the matrix cores, for waves that serve several query heads
+// (D <= 128). Per 32-key block:
 //  * K and V rows are loaded as whole rows (16 lanes x 16 bytes per 256-byte
 //    row, like the VALU form): the MFMA operand layout would have each load
 //    instruction take 64 bytes from each of 16 rows, which streamed ~10 %
 //    slower from HBM. The wave stores both blocks to its LDS area (16-byte
 //    chunks XOR-swizzled by row) and reads the operands back from there;
-//  * S^T = K . Q^T as in split_attend_mfma (16 keys x 16 heads per
-//    v_mfma_f32_16x16x32_f16; K read as lane l: row l % 16 of the half,
-//    chunk 4*kk + l / 16), then the block max and the exponentials, one per
-//    (key, head);
+//  * S^T = K . Q^T, 16 keys x 16 heads per v_mfma_f32_16x16x32 (K read as
+//    lane l: row l % 16 of a 16-key half, chunk 4*kk + l / 16, i.e. dims
+//    32*kk + 8*(l/16) .. +7; Q of head l % 16 for the same dims, zero past
+//    the group); lane l receives S for keys 4*(l/16) .. +3 of head l % 16.
+//    The block max and the exponentials run in that layout, one per (key,
+//    head);
 //  * P^T is already the B operand of O^T = V^T . P^T (heads along N): lane l
 //    holds P of head l % 16 for keys 4*(l/16) + 0..3 of both 16-key halves,
 //    and the MFMA's 32-long contraction takes those 8 keys in that order;
@@ -459,18 +280,23 @@ __device__ __forceinline__ void split_attend_mfma(const DecodeArgs& a, int b, in
 //    dim 16*db + l % 16 of keys 4*(l/16) + 0..3 and of the same keys 16
 //    further;
 //  * O^T accumulates in the MFMA's C layout (lane l: dims 16*db + 4*(l/16) +
-//    0..3 of head l % 16), so the rescale on a new max is lane-local.
+//    0..3 of head l % 16), so the rescale on a new max is lane-local;
+//  * bf16 caches: Q.K^T runs in bf16, and V is converted to fp16 after the
+//    transposing reads (exact in fp16's normal range) for the fp16 P.V.
 // P enters the MFMA as fp16 with 2^kPShift headroom over the running max (so
 // the small weights stay normal); l sums the fp32 weights. At the end O^T goes
 // through LDS to the row layout of split_attend's contract.
 // lw: this wave's LDS scratch, 2 x 32 x D halves (K block, V block; 256-byte aligned).
 constexpr float kPShift = 6.0f;   // P <= 2^(kSlack + kPShift) = 16384 in fp16
 
-__host__ __device__ constexpr bool decode_pv_on_mfma(int d, int g, bool bf16) {
-  return !bf16 && d <= 128 && g >= 4;
+// From 4 heads per wave the per-head dot products, exponentials and output
+// FMAs of the VALU form outweigh the loads (batched long decode: 28/4 heads
+// 1.2x, 32/8 heads 1.1x faster on the matrix cores, fp16 and bf16 alike).
+__host__ __device__ constexpr bool decode_pv_on_mfma(int d, int g, bool /*bf16*/) {
+  return d <= 128 && g >= 4;
 }
 
-template <int D, int G>
+template <int D, int G, bool BF16>
 __device__ __forceinline__ void split_attend_mfma_pv(const DecodeArgs& a, int b, int h0, int lo,
                                                      int hi, int lane, char* lw, float (&m)[G],
                                                      float (&l)[G],
@@ -577,7 +403,7 @@ __device__ __forceinline__ void split_attend_mfma_pv(const DecodeArgs& a, int b,
       s[sb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
-        s[sb] = mfma16<false>(
+        s[sb] = mfma16<BF16>(
             *(const lds_u32x4*)(uintptr_t)((kr0 ^ (unsigned)(kk << 6)) + (unsigned)(sb * 16 * ROWB)),
             qop[kk], s[sb]);
     }
@@ -622,8 +448,14 @@ __device__ __forceinline__ void split_attend_mfma_pv(const DecodeArgs& a, int b,
       const s16x4 hi4 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(vr + 16 * ROWB));
       const f32x2 l2 = __builtin_bit_cast(f32x2, lo4), h2 = __builtin_bit_cast(f32x2, hi4);
-      const u32x4 va = u32x4{__float_as_uint(l2[0]), __float_as_uint(l2[1]),
-                             __float_as_uint(h2[0]), __float_as_uint(h2[1])};
+      u32x4 va = u32x4{__float_as_uint(l2[0]), __float_as_uint(l2[1]),
+                       __float_as_uint(h2[0]), __float_as_uint(h2[1])};
+      if constexpr (BF16) {
+        // bf16 V to fp16 for the fp16 P.V (exact in fp16's normal range)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          va[e] = pack_f16x2(__uint_as_float(va[e] << 16), __uint_as_float(va[e] & 0xffff0000u));
+      }
       oacc[db] = mfma16<false>(va, pb, oacc[db]);
     }
   };
@@ -677,11 +509,10 @@ __device__ __forceinline__ void split_attend_mfma_pv(const DecodeArgs& a, int b,
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the area is reused
 }
 
-// LDS floats per wave that split_run needs: the K and V blocks of the form with
-// P.V on the matrix cores, the P buffer of the form with Q.K^T only, else none.
+// LDS floats per wave that split_run needs: the K and V blocks of the
+// matrix-core form, else none.
 __host__ __device__ constexpr int decode_lds_floats(int d, int g, bool bf16) {
-  return decode_pv_on_mfma(d, g, bf16) ? 2 * 32 * d / 2
-                                       : (decode_uses_mfma(d, g) ? kPRows * kPStride : 1);
+  return decode_pv_on_mfma(d, g, bf16) ? 2 * 32 * d / 2 : 1;
 }
 
 // The split of one wave by whichever form serves its (D, G); pw (this wave's
@@ -691,9 +522,7 @@ __device__ __forceinline__ void split_run(const DecodeArgs& a, int b, int h0, in
                                          int lane, float* pw, float (&m)[G], float (&l)[G],
                                          float (&o)[G][D / lanes_per_row(D)]) {
   if constexpr (decode_pv_on_mfma(D, G, BF16))
-    split_attend_mfma_pv<D, G>(a, b, h0, lo, hi, lane, (char*)pw, m, l, o);
-  else if constexpr (decode_uses_mfma(D, G))
-    split_attend_mfma<D, G, BF16>(a, b, h0, lo, hi, lane, pw, m, l, o);
+    split_attend_mfma_pv<D, G, BF16>(a, b, h0, lo, hi, lane, (char*)pw, m, l, o);
   else
     split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
 }
