@@ -22,8 +22,8 @@
 //    reduced with DPP row permutes, and the online-softmax update is done
 //    once per block and head (section 3.2 of the same page gives the per-row
 //    form: new max, correction factor, exponential, running sum and output);
-//  * from 4 query heads per wave (head_dim <= 128) the per-head work
-//    outweighs the loads and moves to the matrix cores: Q.K^T and P.V
+//  * from 2 query heads per wave (head_dim <= 128) the per-head work
+//    moves to the matrix cores: Q.K^T and P.V
 //    (split_attend_mfma_pv); each K row then serves up to 16 heads in one
 //    16x16x32 MFMA, and the exponentials are spread one per (key, head).
 //
@@ -289,11 +289,14 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // lw: this wave's LDS scratch, 2 x 32 x D halves (K block, V block; 256-byte aligned).
 constexpr float kPShift = 6.0f;   // P <= 2^(kSlack + kPShift) = 16384 in fp16
 
-// From 4 heads per wave the per-head dot products, exponentials and output
-// FMAs of the VALU form outweigh the loads (batched long decode: 28/4 heads
-// 1.2x, 32/8 heads 1.1x faster on the matrix cores, fp16 and bf16 alike).
+// From 2 heads per wave the matrix-core form is the faster one: the VALU
+// form's per-head dot products, exponentials and output FMAs grow with the
+// heads (batched long decode: 28/4 heads 1.2x, 32/8 heads 1.1x, 24/8 heads
+// 1.05x, 16/8 heads 1.03x faster on the matrix cores, fp16 and bf16 alike).
+// One head per wave keeps the VALU form: there the calls are latency-bound
+// and the LDS round trips of the matrix-core form lengthen a wave's chain.
 __host__ __device__ constexpr bool decode_pv_on_mfma(int d, int g, bool /*bf16*/) {
-  return d <= 128 && g >= 4;
+  return d <= 128 && g >= 2;
 }
 
 template <int D, int G, bool BF16>
