@@ -52,7 +52,10 @@
 //    O / l; the row sum l accumulates the fp32 P values;
 //  * the running max is only moved (and O, l rescaled) once a tile max
 //    exceeds it by more than 2^8 — exact, since O and l share the base —
-//    and outputs are referred back to the true row max at the end.
+//    and outputs are referred back to the true row max at the end;
+//  * normalized output without row sums needs no exact max: there a tile's
+//    max is not taken at all, and the base moves (to the row max) only when
+//    a lane's sum of the tile's P exceeds 2^15, which bounds each of those P.
 #include "fa_internal.h"
 
 #include <limits.h>
@@ -79,6 +82,7 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr float kShift = 7.0f;            // log2 of the fp16 headroom factor on P
 constexpr float kSlack = 8.0f;            // stale-max tolerance (log2 units)
+constexpr float kSumCap = 32768.0f;       // tile-sum bound of the max-free softmax (2^15)
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
 
@@ -328,13 +332,17 @@ template <> struct SplitArg<true> { using type = SplitPlan; };
 // VROW: V tiles come straight from V's rows by DMA (fp16 only, head_dim <= 128)
 // and each P.V operand is assembled from two LDS transpose reads, so no V^T
 // pre-pass runs; otherwise they come from the V^T tiles the pre-pass wrote.
-template <int D, bool BF16, bool UNNORM, int HP, bool SPLIT, bool VROW = false>
+// XMAX: the exact running row max is kept, as un-normalized output and row
+// sums need (a.unnorm picks the output form); without it the head_dim <= 128
+// loop skips the per-tile max (the sum-checked base above).
+template <int D, bool BF16, bool XMAX, int HP, bool SPLIT, bool VROW = false>
 __global__ void __launch_bounds__(64 * wg_waves(D, HP)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
                typename SplitArg<SPLIT>::type sp) {
   static_assert(!VROW || (!BF16 && D <= 128), "V rows are read directly for fp16, head_dim <= 128");
   constexpr int kWaves = wg_waves(D, HP);
   constexpr bool PIPE = D <= 128;            // software-pipelined loop (register budget)
+  const bool unnorm = XMAX && a.unnorm != 0;
   constexpr int QG = 4;                      // query groups of 32 rows per head
   static_assert(kWaves == HP * QG, "work-group shape");
   constexpr int kBM = 32 * QG;               // query rows per work-group
@@ -625,8 +633,9 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
     if (needs_mask(t0)) apply_mask(s, t0);
     return rebase(row_max(s));
   };
-  // P = 2^(s*scale*log2e - base) <= 2^(kSlack + kShift) = 32768, packed to fp16.
-  auto expo = [&](const f32x16 (&s)[NKB], float base, u32x4 (&pk)[NKS]) {
+  // P = 2^(s*scale*log2e - base) <= 2^(kSlack + kShift) = 32768, packed to
+  // fp16; returns this lane's sum of the tile's P.
+  auto expo = [&](const f32x16 (&s)[NKB], float base, u32x4 (&pk)[NKS]) -> float {
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -637,7 +646,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
         ls[(i >> 1) & 3] += p0 + p1;
         pk[kb * 2 + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0, p1);
       }
-    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
   // O^T += V^T . P^T over this wave's keys (key order matches the S^T layout).
   auto pv = [&](const char* vst, const u32x4 (&pk)[NKS]) {
@@ -683,19 +692,21 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
     if (ntiles > 0) qk(lds + KST[0], sa);
     __syncthreads();   // K(0) is read everywhere before K(2) overwrites it
     float tm = 0.0f;   // row max of the next tile to exponentiate (log2 units)
+    float base = m_used - kShift;
     if (ntiles > 0) {
       if (needs_mask(tile(0) * BN)) apply_mask(sa, tile(0) * BN);
-      tm = row_max(sa);
+      if constexpr (XMAX) tm = row_max(sa);
     }
 
     auto iter = [&](int t, auto parity, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
       constexpr int P = decltype(parity)::value;
       if (t + 2 < ntiles) issue_k(t + 2, KST[P]);
-      const float base = rebase(tm);
+      if constexpr (XMAX) base = rebase(tm);
       u32x4 pk[NKS];
+      float ts;
       if (t + 1 < ntiles) {
         qk(lds + KST[1 - P], nxt);
-        expo(cur, base, pk);
+        ts = expo(cur, base, pk);
         // Interleave the S(t+1) MFMAs with the exponentials of tile t, with
         // each MFMA's LDS operand read issued three MFMAs ahead of it.
         constexpr int NQ = NKB * NKK, AHEAD = 3;
@@ -707,8 +718,27 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
           __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);     // six VALU
         }
       } else {
-        expo(cur, base, pk);
+        ts = expo(cur, base, pk);
       }
+      if constexpr (!XMAX) {
+        // Max-free softmax: a lane's tile sum bounds each of its P. Above the
+        // cap (or not a number: no base yet, it is still at -1e30) the base
+        // moves to the row max and the tile is exponentiated again; after
+        // that every P <= 2^kShift. Rare after a row's first visible tile.
+        if (__ballot(!(ts <= kSumCap))) {
+          const float nm = fmaxf(m_used, row_max(cur));
+          const float corr = exp2_fast(m_used - nm);
+          m_used = nm;
+          l *= corr;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+          base = m_used - kShift;
+          ts = expo(cur, base, pk);
+        }
+      }
+      l += ts;
       // V(t+1) goes out here rather than with K(t+2): its stage held V(t-1),
       // long consumed, and issuing it mid-tile spreads the DMA over the tile.
       if (t + 1 < ntiles) issue_v(t + 1, VST[1 - P]);
@@ -717,7 +747,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       // tile t+1 is masked first. After the last tile the max is unused.
       if (t + 1 < ntiles && needs_mask(tile(t + 1) * BN)) apply_mask(nxt, tile(t + 1) * BN);
       pv(lds + VST[P], pk);
-      tm = row_max(nxt);
+      if constexpr (XMAX) tm = row_max(nxt);
       {
         // P.V: V^T operand reads four MFMAs ahead; the max's VALU among them.
         // (From V rows an operand takes two transposing reads.)
@@ -727,7 +757,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
         for (int i = 0; i < NP; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
           if (i + AHEAD < NP) __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
+          if constexpr (XMAX) __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
         }
       }
       dma_wait();        // this wave's part of K(t+2), V(t+1) has landed
@@ -760,7 +790,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       }
       const float base = prep(sc, tile(t) * BN);
       u32x4 pk[NKS];
-      expo(sc, base, pk);
+      l += expo(sc, base, pk);
       pv(lds + ST_[ST] + KT, pk);
       {
         constexpr int NP = NKS * NDB, AHEAD = 2;
@@ -791,7 +821,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   float f, lse2, rsum;
   bool merged = false;
   if constexpr (SPLIT) {
-    static_assert(!UNNORM, "the key split merges normalized halves");
+    static_assert(!XMAX, "the key split merges normalized halves");
     __shared__ int split_last;
     if (half >= 0) {
       // This half's normalized partial, O_h = oacc / lt and LSE_h = base +
@@ -865,7 +895,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   } else if (!a.sink_logits) {
     const float to_true = exp2_fast(base - m_true);
     // a row with no visible key (length or window mask) has lt = 0: O = 0, LSE = -inf
-    f = UNNORM ? to_true : (lt > 0.0f ? 1.0f / lt : 0.0f);
+    f = unnorm ? to_true : (lt > 0.0f ? 1.0f / lt : 0.0f);
     lse2 = base + __log2f(lt);
     rsum = lt * to_true;
   } else {
@@ -879,13 +909,13 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
                            : mx + __log2f(exp2_fast(lns - mx) + exp2_fast(sg - mx));
     const float mr = fmaxf(m_true, sg);
     const float to_ref = lt > 0.0f ? exp2_fast(base - mr) : 0.0f;
-    f = UNNORM ? to_ref : (lt > 0.0f ? exp2_fast(base - lse2) : 0.0f);
+    f = unnorm ? to_ref : (lt > 0.0f ? exp2_fast(base - lse2) : 0.0f);
     rsum = lt * to_ref + exp2_fast(sg - mr);
   }
   if (hh == 0 && q_valid) {
     const int64_t ri = ((int64_t)b * a.n_heads_q + h) * a.seqlen_q + qi;
     a.lse[ri] = lse2 * kLn2;
-    if (a.row_sum) a.row_sum[ri] = rsum;
+    if (XMAX && a.row_sum) a.row_sum[ri] = rsum;   // the launcher picks XMAX for row sums
   }
 
   // Stage this wave's 32 output rows in LDS ([row][D] fp32, 16-byte chunks
@@ -1213,10 +1243,12 @@ hipError_t launch_attn_d(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hi
   // L2 at a few thousand keys, so its groups run one at a time per XCD.
   constexpr int kSlots = 32 * 2;   // two work-groups per compute unit
   a.wg_serial = D == 256 && wg_serial_fits(a.batch * a.n_heads_kv, per_group, nqb, kSlots) ? kSlots : 0;
+  a.unnorm = unnorm;
+  const bool xmax = unnorm || a.row_sum;   // the exact row max is kept for these outputs
   const auto go = [&](auto hp_c) {
     constexpr int HP = decltype(hp_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
-    if (unnorm)
+    if (xmax)
       hipLaunchKernelGGL((prefill_kernel<D, BF16, true, HP, false>), grid,
                          dim3(64 * wg_waves(D, HP)), 0, stream, a, (const unsigned short*)w.ws,
                          NoSplit{});
@@ -1237,14 +1269,17 @@ hipError_t launch_attn_d(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hi
 
 // The attention launch reading V's rows directly (fp16, head_dim <= 128).
 template <int D>
-hipError_t launch_attn_vrow_d(const PrefillArgs& a, bool unnorm, hipStream_t stream) {
+hipError_t launch_attn_vrow_d(const PrefillArgs& a0, bool unnorm, hipStream_t stream) {
   constexpr int BM = block_rows(D);
-  const int per_group = a.n_heads_q / a.n_heads_kv;
-  const int nqb = (a.seqlen_q + BM - 1) / BM;
+  const int per_group = a0.n_heads_q / a0.n_heads_kv;
+  const int nqb = (a0.seqlen_q + BM - 1) / BM;
+  PrefillArgs a = a0;
+  a.unnorm = unnorm;
+  const bool xmax = unnorm || a.row_sum;   // the exact row max is kept for these outputs
   const auto go = [&](auto hp_c) {
     constexpr int HP = decltype(hp_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
-    if (unnorm)
+    if (xmax)
       hipLaunchKernelGGL((prefill_kernel<D, false, true, HP, false, true>), grid,
                          dim3(64 * wg_waves(D, HP)), 0, stream, a, nullptr, NoSplit{});
     else
