@@ -310,6 +310,15 @@ int fa_prefill_split_units(int batch, int seqlen_q, int seqlen_kv, int n_heads_q
   return n;
 }
 
+int fa_prefill_trio(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                    int head_dim, int causal, int window) {
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_kv <= 0 || n_heads_q <= 0 || n_heads_kv <= 0 ||
+      n_heads_q % n_heads_kv != 0 || window < 0)
+    return -fail(FA_ERR_INVALID_ARG, "fa_prefill_trio: invalid sizes");
+  return fa::prefill_trio(batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv, head_dim, causal,
+                          window) ? 1 : 0;
+}
+
 int fa_attn_merge(const float* o_a, int64_t oa_sb, int64_t oa_ss, int64_t oa_sh,
                   const float* lse_a, const float* o_b, int64_t ob_sb, int64_t ob_ss,
                   int64_t ob_sh, const float* lse_b, const float* sink_logits, int batch,

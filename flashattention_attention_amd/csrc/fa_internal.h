@@ -134,6 +134,10 @@ hipError_t launch_prefill_attn(const PrefillArgs& a, const VtArgs& w, int head_d
 // One launch reading V's rows directly (no V^T workspace): fp16 inputs at
 // head_dim 64 or 128, where prefill_reads_v_rows is true.
 bool prefill_reads_v_rows(int head_dim, bool bf16);
+// Whether the attention launch of the two-launch prefill runs three work-groups
+// per compute unit (32-key tiles) for this shape instead of two.
+bool prefill_trio(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                  int head_dim, int causal, int window);
 hipError_t launch_prefill_attn_vrow(const PrefillArgs& a, int head_dim, bool unnormalized,
                                     hipStream_t stream);
 // The same with the key split (sp.n_units > 0); head_dim 64 or 128, normalized output.

@@ -165,17 +165,19 @@ __device__ __forceinline__ void dma16_at(const void* base, unsigned lane_bytes, 
 
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// V^T tile layout: D rows (head dims) x BN keys of fp16, BN*2 bytes per row
-// in 16-byte chunks. Chunk c holds keys 16*(c/2) + 4*(c%2) + {0,1,2,3} and
-// 16*(c/2) + 8 + 4*(c%2) + {0,1,2,3}: the key order in which the S^T
-// accumulator hands P to the P.V contraction, so one 16-byte read is one MFMA
-// operand. Chunks are XOR-swizzled by row so that the 32 rows read together
-// by an MFMA operand load fall on distinct banks.
-template <int BN>
+// V^T tile layout: BN keys of D head dims in fp16, stored as BN / 32 halves
+// of 32 keys, each D rows (head dims) x 64 bytes of 16-byte chunks. Chunk c
+// of a half holds its keys 16*(c/2) + 4*(c%2) + {0,1,2,3} and 16*(c/2) + 8 +
+// 4*(c%2) + {0,1,2,3}: the key order in which the S^T accumulator hands P to
+// the P.V contraction, so one 16-byte read is one MFMA operand. Chunks are
+// XOR-swizzled by row so that the rows read together by an MFMA operand load
+// fall on distinct banks. A 64-key tile is two 32-key tiles back to back, so
+// kernels with 32-key tiles can read either half of it as a tile of their own.
+constexpr int kVtRowBytes = 64;   // bytes per V^T row of a 32-key half
+template <int BN, int D>
 __device__ __forceinline__ int vt_chunk_offset(int d, int c) {
-  if constexpr (BN == 128) return d * 256 + ((c ^ (d & 15)) << 4);
-  else if constexpr (BN == 64) return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
-  else return d * 64 + ((c ^ ((d >> 2) & 3)) << 4);
+  static_assert(BN == 32 || BN == 64, "tile sizes");
+  return (c >> 2) * (D * kVtRowBytes) + d * kVtRowBytes + (((c & 3) ^ ((d >> 2) & 3)) << 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -219,8 +221,8 @@ vt_pack_kernel(const unsigned short* __restrict__ v, int64_t v_sb, int64_t v_ss,
       lo[j] = __builtin_amdgcn_perm(row[2 * j + 1][e], row[2 * j][e], 0x05040100u);
       hi[j] = __builtin_amdgcn_perm(row[2 * j + 1][e], row[2 * j][e], 0x07060302u);
     }
-    *(u32x4*)(out + vt_chunk_offset<BN>(d0 + 2 * e, c)) = lo;
-    *(u32x4*)(out + vt_chunk_offset<BN>(d0 + 2 * e + 1, c)) = hi;
+    *(u32x4*)(out + vt_chunk_offset<BN, D>(d0 + 2 * e, c)) = lo;
+    *(u32x4*)(out + vt_chunk_offset<BN, D>(d0 + 2 * e + 1, c)) = hi;
   }
 }
 
@@ -333,20 +335,26 @@ template <> struct SplitArg<true> { using type = SplitPlan; };
 // and each P.V operand is assembled from two LDS transpose reads, so no V^T
 // pre-pass runs; otherwise they come from the V^T tiles the pre-pass wrote.
 // XMAX: the exact running row max is kept, as un-normalized output and row
-// sums need (a.unnorm picks the output form); without it the head_dim <= 128
-// loop skips the per-tile max (the sum-checked base above).
-template <int D, bool BF16, bool XMAX, int HP, bool SPLIT, bool VROW = false>
-__global__ void __launch_bounds__(64 * wg_waves(D, HP)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// sums need (a.unnorm picks the output form); without it the loop skips the
+// per-tile max (the sum-checked base above).
+// TRIO (head_dim 128, one query head per work-group): three work-groups per
+// compute unit instead of two — 32-key tiles, no software pipeline, O staged
+// in two halves — for grids of equal-length blocks that overflow one round of
+// two per compute unit (see prefill_trio).
+template <int D, bool BF16, bool XMAX, int HP, bool SPLIT, bool VROW = false, bool TRIO = false>
+__global__ void __launch_bounds__(64 * wg_waves(D, HP))
+__attribute__((amdgpu_waves_per_eu(TRIO ? 3 : 2, TRIO ? 3 : 2)))
 prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
                typename SplitArg<SPLIT>::type sp) {
   static_assert(!VROW || (!BF16 && D <= 128), "V rows are read directly for fp16, head_dim <= 128");
+  static_assert(!TRIO || (D == 128 && HP == 1 && !SPLIT && !VROW), "three-per-CU form");
   constexpr int kWaves = wg_waves(D, HP);
-  constexpr bool PIPE = D <= 128;            // software-pipelined loop (register budget)
+  constexpr bool PIPE = D <= 128 && !TRIO;   // software-pipelined loop (register budget)
   const bool unnorm = XMAX && a.unnorm != 0;
   constexpr int QG = 4;                      // query groups of 32 rows per head
   static_assert(kWaves == HP * QG, "work-group shape");
   constexpr int kBM = 32 * QG;               // query rows per work-group
-  constexpr int BN = tile_keys(D);           // keys per tile
+  constexpr int BN = TRIO ? 32 : tile_keys(D);   // keys per tile
   constexpr int NKB = BN / 32;               // 32-key MFMA blocks per tile
   constexpr int NKS = BN / 16;               // MFMA k-steps of P.V per tile
   constexpr int NKK = D / 16;                // MFMA k-steps of Q.K^T
@@ -369,7 +377,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
 
   // K/V^T tiles (two stages); after the loop, the per-wave O staging area
   // (32 rows x D / OH fp32 per wave).
-  constexpr int OH = D > 128 ? 2 : 1;        // O rows staged in OH parts of D / OH dims
+  constexpr int OH = D > 128 || TRIO ? 2 : 1;   // O rows staged in OH parts of D / OH dims
   constexpr int DP = D / OH;
   constexpr int OSTG = 32 * DP * 4;
   constexpr int LDS_BYTES = kWaves * OSTG > 2 * STAGE ? kWaves * OSTG : 2 * STAGE;
@@ -439,7 +447,11 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       ntiles -= n0;
     }
   }
-  const int ntiles_all = (a.seqlen_kv + BN - 1) / BN;
+  // V^T tiles as the pre-pass wrote them (tile_keys(D) keys each; the TRIO
+  // form reads its 32-key tiles as halves of them).
+  constexpr int BNP = tile_keys(D);
+  constexpr int VTP = D * BNP * 2;
+  const int ntiles_all = (a.seqlen_kv + BNP - 1) / BNP;
   const int wave_first_qpos = q0 + qw * 32 + off;
   // Absolute index of the t-th tile the loop visits (the serial order walks
   // every second group's tiles backwards; the online softmax takes the tiles
@@ -450,7 +462,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
 
   const unsigned short* kp =
       (const unsigned short*)a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
-  const char* vtp = (const char*)vt_ws + ((int64_t)b * a.n_heads_kv + hk) * ntiles_all * VT;
+  const char* vtp = (const char*)vt_ws + ((int64_t)b * a.n_heads_kv + hk) * ntiles_all * VTP;
   const unsigned short* vp =
       (const unsigned short*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
 
@@ -522,9 +534,22 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       }
       return;
     }
-    const char* base = vtp + (int64_t)tile(t) * VT;
     unsigned ln = (unsigned)lane;
     asm volatile("" : "+v"(ln));
+    if constexpr (TRIO) {
+      // 32-key tile t is half t & 1 of 64-key pre-pass tile t / 2 (the halves
+      // lie back to back in the same layout as a 32-key tile).
+      static_assert(BNP == 64 && BN == 32 && VTP == 2 * VT, "halves of 64-key tiles");
+      const int tt = tile(t);
+      const char* base = vtp + (int64_t)(tt >> 1) * VTP + (tt & 1) * VT;
+#pragma unroll
+      for (int j = 0; j < V_INSTR; ++j) {
+        const int J = wave * V_INSTR + j;
+        dma16_at(base + J * 1024, ln << 4, lds_base + dst + J * 1024);
+      }
+      return;
+    }
+    const char* base = vtp + (int64_t)tile(t) * VT;
 #pragma unroll
     for (int j = 0; j < V_INSTR; ++j) {
       const int J = wave * V_INSTR + j;
@@ -545,7 +570,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   int va_off[NKS];   // + db * 32 rows for head-dim block db (the swizzle repeats every 16 rows)
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
-    va_off[ks] = vt_chunk_offset<BN>(n, ks * 2 + hh);
+    va_off[ks] = vt_chunk_offset<BN, D>(n, ks * 2 + hh);
   // VROW: the byte offset, in a V-row stage, of this lane's first transpose read
   // for head-dim block db at k-step 0. Lane j of a 16-lane group g points at
   // the 4 dims m0 + 4 (j % 4) .. + 3 (m0 = 32 db + 16 (g & 1)) of key 4 hh +
@@ -648,6 +673,24 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       }
     return (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
+  // Max-free softmax (!XMAX): a lane's tile sum ts bounds each of its P. Above
+  // the cap (or not a number: no base yet, it is still at -1e30) the base
+  // moves to the row max and the tile is exponentiated again; after that
+  // every P <= 2^kShift. Rare after a row's first visible tile.
+  auto sum_check = [&](const f32x16 (&s)[NKB], float& base, float& ts, u32x4 (&pk)[NKS]) {
+    if (__ballot(!(ts <= kSumCap))) {
+      const float nm = fmaxf(m_used, row_max(s));
+      const float corr = exp2_fast(m_used - nm);
+      m_used = nm;
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+      base = m_used - kShift;
+      ts = expo(s, base, pk);
+    }
+  };
   // O^T += V^T . P^T over this wave's keys (key order matches the S^T layout).
   auto pv = [&](const char* vst, const u32x4 (&pk)[NKS]) {
 #pragma unroll
@@ -666,7 +709,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
           va = u32x4{__float_as_uint(l2[0]), __float_as_uint(l2[1]), __float_as_uint(h2[0]),
                      __float_as_uint(h2[1])};
         } else {
-          va = *(const u32x4*)(vst + va_off[ks] + db * 32 * (BN * 2));
+          va = *(const u32x4*)(vst + va_off[ks] + db * 32 * kVtRowBytes);
         }
         oacc[db] = mfma_pv(va, pk[ks], oacc[db]);
       }
@@ -720,24 +763,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       } else {
         ts = expo(cur, base, pk);
       }
-      if constexpr (!XMAX) {
-        // Max-free softmax: a lane's tile sum bounds each of its P. Above the
-        // cap (or not a number: no base yet, it is still at -1e30) the base
-        // moves to the row max and the tile is exponentiated again; after
-        // that every P <= 2^kShift. Rare after a row's first visible tile.
-        if (__ballot(!(ts <= kSumCap))) {
-          const float nm = fmaxf(m_used, row_max(cur));
-          const float corr = exp2_fast(m_used - nm);
-          m_used = nm;
-          l *= corr;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
-          base = m_used - kShift;
-          ts = expo(cur, base, pk);
-        }
-      }
+      if constexpr (!XMAX) sum_check(cur, base, ts, pk);
       l += ts;
       // V(t+1) goes out here rather than with K(t+2): its stage held V(t-1),
       // long consumed, and issuing it mid-tile spreads the DMA over the tile.
@@ -771,6 +797,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
     // Plain double buffer: tile t+1 (K and V^T together) arrives while tile t
     // is computed from the other stage.
     constexpr unsigned ST_[2] = {0, STAGE};
+    float lbase = m_used - kShift;   // the base of the max-free softmax
     auto step = [&](int t, auto stage) {
       constexpr int ST = decltype(stage)::value;
       if (t + 1 < ntiles) { issue_k(t + 1, ST_[1 - ST]); issue_v(t + 1, ST_[1 - ST] + KT); }
@@ -788,9 +815,16 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
           if (i + AHEAD < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
       }
-      const float base = prep(sc, tile(t) * BN);
+      float base = lbase;
+      if constexpr (XMAX) {
+        base = prep(sc, tile(t) * BN);
+      } else if (needs_mask(tile(t) * BN)) {
+        apply_mask(sc, tile(t) * BN);
+      }
       u32x4 pk[NKS];
-      l += expo(sc, base, pk);
+      float ts = expo(sc, base, pk);
+      if constexpr (!XMAX) sum_check(sc, lbase, ts, pk);
+      l += ts;
       pv(lds + ST_[ST] + KT, pk);
       {
         constexpr int NP = NKS * NDB, AHEAD = 2;
@@ -1066,7 +1100,7 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
   for (int k8 = 0; k8 < 8; ++k8) ka8[k8] = n * KROW + (((2 * k8 + hh) ^ (n & 15)) << 4);
   int va_off[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) va_off[ks] = dh * DH * (BN * 2) + vt_chunk_offset<BN>(n, 2 * ks + hh);
+  for (int ks = 0; ks < NKS; ++ks) va_off[ks] = dh * DH * kVtRowBytes + vt_chunk_offset<BN, 512>(n, 2 * ks + hh);
 
   float m_used = -1e30f, m_true = -1e30f, l = 0.0f;
   f32x16 oacc[NDB];
@@ -1137,7 +1171,7 @@ prefill512_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        oacc[db] = mfma_pv(*(const u32x4*)(vst + va_off[ks] + db * 32 * (BN * 2)), pk[ks],
+        oacc[db] = mfma_pv(*(const u32x4*)(vst + va_off[ks] + db * 32 * kVtRowBytes), pk[ks],
                            oacc[db]);
     constexpr int NP = NKS * NDB;
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
@@ -1245,25 +1279,34 @@ hipError_t launch_attn_d(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hi
   a.wg_serial = D == 256 && wg_serial_fits(a.batch * a.n_heads_kv, per_group, nqb, kSlots) ? kSlots : 0;
   a.unnorm = unnorm;
   const bool xmax = unnorm || a.row_sum;   // the exact row max is kept for these outputs
-  const auto go = [&](auto hp_c) {
+  const auto go = [&](auto hp_c, auto trio_c) {
     constexpr int HP = decltype(hp_c)::value;
+    constexpr bool TRIO = decltype(trio_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
     if (xmax)
-      hipLaunchKernelGGL((prefill_kernel<D, BF16, true, HP, false>), grid,
+      hipLaunchKernelGGL((prefill_kernel<D, BF16, true, HP, false, false, TRIO>), grid,
                          dim3(64 * wg_waves(D, HP)), 0, stream, a, (const unsigned short*)w.ws,
                          NoSplit{});
     else
-      hipLaunchKernelGGL((prefill_kernel<D, BF16, false, HP, false>), grid,
+      hipLaunchKernelGGL((prefill_kernel<D, BF16, false, HP, false, false, TRIO>), grid,
                          dim3(64 * wg_waves(D, HP)), 0, stream, a, (const unsigned short*)w.ws,
                          NoSplit{});
   };
+  using no = std::false_type;
   if constexpr (D <= 128) {
     if (per_group % 2 == 0) {
-      go(std::integral_constant<int, 2>{});
+      go(std::integral_constant<int, 2>{}, no{});
       return hipGetLastError();
     }
   }
-  go(std::integral_constant<int, 1>{});
+  if constexpr (D == 128) {
+    if (prefill_trio(a.batch, a.seqlen_q, a.seqlen_kv, a.n_heads_q, a.n_heads_kv, D, a.causal,
+                     a.window)) {
+      go(std::integral_constant<int, 1>{}, std::true_type{});
+      return hipGetLastError();
+    }
+  }
+  go(std::integral_constant<int, 1>{}, no{});
   return hipGetLastError();
 }
 
@@ -1527,6 +1570,34 @@ hipError_t launch_prefill_pack(const PrefillArgs& a, const VtArgs& w, int head_d
 }
 
 bool prefill_reads_v_rows(int head_dim, bool bf16) { return !bf16 && head_dim <= 128; }
+
+bool prefill_trio(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                  int head_dim, int causal, int window) {
+  // Three work-groups per compute unit pay off when the blocks are of about
+  // equal length and the grid overflows one round of two per compute unit
+  // (512 slots) but fits one round of three (768): two per compute unit would
+  // end with a partly filled second round. Unequal (causal) blocks keep two
+  // per compute unit: there the longest blocks set the end, and they run
+  // faster with one neighbour than with two.
+  constexpr int kCUs = 256, BM = 128, BNP = 64;
+  if (head_dim != 128 || n_heads_kv <= 0 || (n_heads_q / n_heads_kv) % 2 == 0) return false;
+  const int nqb = (seqlen_q + BM - 1) / BM;
+  const int64_t wgs = (int64_t)batch * n_heads_q * nqb;
+  if (wgs <= 2 * kCUs || wgs > 3 * kCUs) return false;
+  const int off = seqlen_kv - seqlen_q;
+  int64_t sum = 0;
+  int most = 0;
+  for (int qb = 0; qb < nqb; ++qb) {   // key tiles of each block, as the kernel counts them
+    const int q0 = qb * BM;
+    int kv_end = seqlen_kv;
+    if (causal) kv_end = std::min(kv_end, std::min(q0 + BM, seqlen_q) + off);
+    const int kv_lo = window > 0 ? std::max(0, q0 + off - window + 1) : 0;
+    const int n = kv_end > kv_lo ? (kv_end + BNP - 1) / BNP - kv_lo / BNP : 0;
+    sum += n;
+    most = std::max(most, n);
+  }
+  return sum > 0 && 4 * (int64_t)most * nqb <= 5 * sum;   // longest block <= 1.25 x the mean
+}
 
 hipError_t launch_prefill_attn_vrow(const PrefillArgs& a, int head_dim, bool unnormalized,
                                     hipStream_t stream) {

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "fa_prefill_split_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
     "fa_prefill_split_units": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                 ctypes.POINTER(ctypes.c_uint16), _i32], _i32),
+    "fa_prefill_trio": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _i32),
     "fa_attn_merge": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                        _i32, _i32, _i32, _i32, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "fa_prefill_workspace_size": ([_i32, _i32, _i32, _i32], ctypes.c_uint64),
@@ -427,6 +428,16 @@ def prefill_split_units(batch: int, seqlen_q: int, seqlen_kv: int, n_heads_q: in
                                    1 if causal else 0, window, buf, 512)
     _check(-n if n < 0 else 0, "fa_prefill_split_units")
     return [(buf[i] & 0x3FFF, buf[i] >> 14) for i in range(n)]
+
+
+def prefill_trio(batch: int, seqlen_q: int, seqlen_kv: int, n_heads_q: int, n_heads_kv: int,
+                 head_dim: int, causal: bool = True, window: int = 0) -> bool:
+    """Whether the two-launch prefill's attention runs three work-groups per
+    compute unit for this shape (host only)."""
+    r = load_library().fa_prefill_trio(batch, seqlen_q, seqlen_kv, n_heads_q, n_heads_kv,
+                                       head_dim, 1 if causal else 0, window)
+    _check(-r if r < 0 else 0, "fa_prefill_trio")
+    return r == 1
 
 
 def decode_plan(kv_lens: Sequence[int], n_heads_q: int, n_heads_kv: int, head_dim: int,

@@ -255,6 +255,28 @@ int fa_prefill_split_units(int batch, int seqlen_q, int seqlen_kv, int n_heads_q
                            int head_dim, int causal, int window, uint16_t* units, int max_units);
 
 /*
+ * fa_prefill_trio — whether the attention launch of fa_prefill_fwd_packed
+ * (and of fa_prefill_fwd where it repacks V: bf16 inputs) runs three
+ * work-groups per compute unit for a shape (host only; for inspection and
+ * tests). Results are the same attention either way, within rounding.
+ *
+ * Source: "60 · r57 — FA KV staging double buffering (REVERTED)", section 1
+ * (the grid over query blocks and heads); "STAGE_D.md — FMHA Kernel
+ * Development", D3/D4 (the sliding-window branch, whose blocks all see about
+ * the same number of keys).
+ *
+ * The three-per-CU form (32-key tiles, no software pipeline; head_dim 128,
+ * an odd number of query heads per KV head) is chosen when the grid's
+ * 128-row blocks carry about equal numbers of key tiles (the longest at most
+ * 1.25x the mean, counted at full lengths) and there are more blocks than
+ * two per compute unit hold (512) but no more than three do (768).
+ * Returns 1 (three per CU) or 0 (two); -FA_ERR_INVALID_ARG for
+ * non-positive sizes, bad head counts or window < 0.
+ */
+int fa_prefill_trio(int batch, int seqlen_q, int seqlen_kv, int n_heads_q, int n_heads_kv,
+                    int head_dim, int causal, int window);
+
+/*
  * fa_attn_merge — merge two attention passes over disjoint key sets, and an
  * optional per-head sink, through their LSEs.
  *

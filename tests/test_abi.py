@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
                           "fa_decode_fused_workspace_size", "fa_decode_fused_waves",
                           "fa_attn_merge", "fa_prefill_fwd_packed_split",
                           "fa_prefill_split_workspace_size", "fa_prefill_split_units",
-                          "fa_status_string", "fa_last_error"}
+                          "fa_prefill_trio", "fa_status_string", "fa_last_error"}
     lib = ctypes.CDLL(fa.library_path())
     for name in names:
         assert hasattr(lib, name), name

@@ -50,18 +50,27 @@ def test_prefill_kernels_run_two_waves_without_scratch():
     ks = _pick(rep, "prefill_kernelILi64E", "prefill_kernelILi128E", "prefill_kernelILi256E",
                "prefill512_kernel")
     # head_dim 64 and 128: {bf16, fp16} x {normalized, un-normalized} x {1, 2 heads},
-    # plus the key-split form ({bf16, fp16} x {1, 2 heads}, normalized) and the
-    # fp16 form that reads V's rows ({normalized, un-normalized} x {1, 2 heads});
+    # plus the key-split form ({bf16, fp16} x {1, 2 heads}, normalized), the
+    # fp16 form that reads V's rows ({normalized, un-normalized} x {1, 2 heads})
+    # and, at head_dim 128 with one head per work-group, the three-per-CU form
+    # ({bf16, fp16} x {normalized, un-normalized});
     # head_dim 256 and 512: {bf16, fp16} x {normalized, un-normalized}
-    # (template arguments: D, bf16, un-normalized, heads, split, V rows)
-    assert len(ks) == 40, sorted(ks)
-    assert len([k for k in ks if "ELb1ELb0EEEvNS" in k]) == 8, sorted(ks)
-    vrow = [k for k in ks if "ELb0ELb1EEEvNS" in k]
+    # (template arguments: D, bf16, exact max, heads, split, V rows, three per CU)
+    assert len(ks) == 44, sorted(ks)
+    assert len([k for k in ks if "ELb1ELb0ELb0EEEvNS" in k]) == 8, sorted(ks)
+    vrow = [k for k in ks if "ELb0ELb1ELb0EEEvNS" in k]
     assert len(vrow) == 8 and all("ILi64ELb0E" in k or "ILi128ELb0E" in k for k in vrow), vrow
+    trio = [k for k in ks if "ELb0ELb0ELb1EEEvNS" in k]
+    assert len(trio) == 4 and all("ILi128E" in k and "ELi1ELb0ELb0ELb1EEEvNS" in k
+                                  for k in trio), trio
     for name, r in ks.items():
         assert r["scratch_bytes"] == 0 and r["vgpr_spill"] == 0, (name, r)
-        assert r["waves_per_simd"] == 2, (name, r)
-        assert r["lds_bytes"] <= 160 * 1024, (name, r)
+        if name in trio:
+            # three work-groups of four waves per compute unit
+            assert r["waves_per_simd"] == 3 and r["lds_bytes"] <= 160 * 1024 // 3, (name, r)
+        else:
+            assert r["waves_per_simd"] == 2, (name, r)
+            assert r["lds_bytes"] <= 160 * 1024, (name, r)
     # head_dim 256 keeps its tile stages and O staging within 80 KB, so two
     # work-groups share a compute unit
     for name, r in _pick(rep, "prefill_kernelILi256E").items():
