@@ -110,7 +110,10 @@ def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None, split=False):
     B, Sq, Hq, D = x["q"].shape
     o = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
-    rs = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    # row sums only where the workload asks for them (un-normalized output):
+    # the others state O and the LSE as their outputs
+    rs = (torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+          if cfg.out_unnormalized else None)
 
     ws = torch.empty(fa.prefill_workspace_size(B, cfg.seqlen_kv, cfg.n_heads_kv, D),
                      dtype=torch.uint8, device="cuda")
@@ -121,7 +124,7 @@ def prefill_setup(torch, fa, cfg, sink_logits=None, tensors=None, split=False):
     if split:
         sws = torch.zeros(fa.prefill_split_workspace_size(B, Sq, Hq, D), dtype=torch.uint8,
                           device="cuda")
-        rs = None   # row sums turn the split off
+        rs = None   # (row sums would turn the split off)
     pack = fa.prefill_pack_v(v, workspace=ws, prepare=True)
     attn = fa.prefill_packed(q, k, ws, causal=cfg.causal, softmax_scale=cfg.scale,
                              out_unnormalized=cfg.out_unnormalized, out=o, lse=lse, row_sum=rs,
