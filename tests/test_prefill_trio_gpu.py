@@ -57,6 +57,8 @@ CASES = [
     (1, 1024, 1024, 70, 10, "bf16", True, False, None, 256, True, 1.0, None),  # window + sinks
     (2, 1024, 1024, 42, 6, "f16", True, False, [1024, 700], 256, False, 4.0, None),
     (3, 77, 5000, 189, 27, "bf16", True, False, None, 0, False, 1.0, [0, 38, 76]),
+    (2, 129, 129, 140, 20, "bf16", False, False, [0, 77], 0, False, 1.0, None),  # empty sequence
+    (2, 200, 300, 140, 20, "f16", True, False, [300, 150], 5000, True, 2.0, None),  # window > S
 ]
 
 
