@@ -747,9 +747,18 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       if constexpr (XMAX) base = rebase(tm);
       u32x4 pk[NKS];
       float ts;
-      if (t + 1 < ntiles) {
-        qk(lds + KST[1 - P], nxt);
-        ts = expo(cur, base, pk);
+      // S(t+1) = K(t+1).Q^T on the matrix cores while the VALU turns S(t)
+      // into P(t). After the last tile the product is computed anyway, from
+      // whatever the other K stage holds, and never used: a branch around it
+      // would split this block, and the compiler then hoists the scaling FMAs
+      // of the exponentials out of it, away from the MFMAs.
+      qk(lds + KST[1 - P], nxt);
+      ts = expo(cur, base, pk);
+      // The packs of P stay among the MFMAs (the compiler would otherwise sink
+      // them past the sum check below, whose rare branch rewrites P).
+#pragma unroll
+      for (int i = 0; i < NKS; ++i) asm volatile("" ::"v"(pk[i]));
+      {
         // Interleave the S(t+1) MFMAs with the exponentials of tile t, with
         // each MFMA's LDS operand read issued three MFMAs ahead of it.
         constexpr int NQ = NKB * NKK, AHEAD = 3;
@@ -760,8 +769,6 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
           if (i + AHEAD < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);     // six VALU
         }
-      } else {
-        ts = expo(cur, base, pk);
       }
       if constexpr (!XMAX) sum_check(cur, base, ts, pk);
       l += ts;
