@@ -467,6 +467,13 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       (const unsigned short*)a.v + (int64_t)b * a.v_sb + (int64_t)hk * a.v_sh;
 
   const unsigned lds_base = (unsigned)(uintptr_t)(lptr_t)lds;
+  // Row addressing of the DMAs of whole tiles: one 64-bit multiply per tile
+  // for this wave's first row, then a fixed step per instruction (RPI rows),
+  // all in scalar registers.
+  const int64_t k_row2 = a.k_ss * 2, v_row2 = a.v_ss * 2;           // bytes per K / V row
+  const char* kp_w = (const char*)kp + (int64_t)wave * K_INSTR * RPI * k_row2;
+  const char* vp_w = (const char*)vp + (int64_t)wave * V_INSTR * RPI * v_row2;
+  const int64_t k_step = (int64_t)RPI * k_row2, v_step = (int64_t)RPI * v_row2;
 
   // DMA of this wave's share of the K rows / V^T bytes of tile tile(t) to LDS
   // offset dst. DMA instruction j of a wave writes rows R0 .. R0 + RPI - 1 of
@@ -486,11 +493,13 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
     const unsigned lc16 = ((ln % CPR) ^ (lrow & SWZ)) << 4;
     if (t0 + BN <= a.seqlen_kv) {
       const unsigned lrow_b = lrow * (unsigned)a.k_ss * 2u;   // < 2^31 (k_ss <= 2^23)
+      const char* rb = kp_w + (int64_t)t0 * k_row2;
 #pragma unroll
       for (int j = 0; j < K_INSTR; ++j) {
         const int r0 = (wave * K_INSTR + j) * RPI;
-        dma16_at(kp + (int64_t)(t0 + r0) * a.k_ss, (lc16 ^ ((unsigned)(r0 & SWZ) << 4)) + lrow_b,
+        dma16_at(rb, (lc16 ^ ((unsigned)(r0 & SWZ) << 4)) + lrow_b,
                  lds_base + dst + (wave * K_INSTR + j) * 1024);
+        rb += k_step;
       }
     } else {
 #pragma unroll
@@ -517,11 +526,11 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       const unsigned lc16 = ((ln % CPR) ^ (unsigned)vswz((int)lrow)) << 4;
       if (t0 + BN <= a.seqlen_kv) {
         const unsigned lrow_b = lrow * (unsigned)a.v_ss * 2u;   // < 2^31 (v_ss <= 2^23)
+        const char* rb = vp_w + (int64_t)t0 * v_row2;
 #pragma unroll
         for (int j = 0; j < V_INSTR; ++j) {
-          const int r0 = (wave * V_INSTR + j) * RPI;
-          dma16_at(vp + (int64_t)(t0 + r0) * a.v_ss, lc16 + lrow_b,
-                   lds_base + dst + (wave * V_INSTR + j) * 1024);
+          dma16_at(rb, lc16 + lrow_b, lds_base + dst + (wave * V_INSTR + j) * 1024);
+          rb += v_step;
         }
       } else {
 #pragma unroll
