@@ -366,8 +366,17 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   constexpr int CPR = D / 8;                 // 16-byte chunks per K row
   constexpr int RPI = 64 / CPR;              // K rows per 1 KB DMA instruction
   constexpr int SWZ = CPR < 16 ? CPR - 1 : 15;
-  constexpr int K_INSTR = KT / 1024 / kWaves;   // DMA instructions per wave per tile
-  constexpr int V_INSTR = VT / 1024 / kWaves;
+  // Two query heads per work-group (HP = 2): the second team of four waves
+  // runs half a tile behind the first, so the two waves that share a SIMD
+  // are in opposite phases (one turns S into P on the VALU while the other's
+  // P.V keeps the matrix core busy). The leading team issues all the DMAs.
+  // (The fp16 form that reads V rows keeps both teams in step: staggered, it
+  // spills. The exact-max form keeps them in step too: staggered, it ran
+  // 1-2 % slower.)
+  constexpr bool STAG = HP == 2 && D <= 128 && !TRIO && !SPLIT && !VROW && !XMAX;
+  constexpr int kDmaWaves = STAG ? QG : kWaves;
+  constexpr int K_INSTR = KT / 1024 / kDmaWaves;   // DMA instructions per wave per tile
+  constexpr int V_INSTR = VT / 1024 / kDmaWaves;
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile too small for the DMA split");
   // Row swizzle of V rows in LDS (VROW): one transpose read takes 64 bytes
   // (4 chunks) from each of 4 consecutive rows; XOR-ing the chunk index with
@@ -375,12 +384,13 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   // per bank line) puts the four rows on distinct banks.
   constexpr auto vswz = [](int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); };
 
-  // K/V^T tiles (two stages); after the loop, the per-wave O staging area
-  // (32 rows x D / OH fp32 per wave).
+  // K/V^T tiles (two stages; three V^T stages with staggered teams); after
+  // the loop, the per-wave O staging area (32 rows x D / OH fp32 per wave).
   constexpr int OH = D > 128 || TRIO ? 2 : 1;   // O rows staged in OH parts of D / OH dims
   constexpr int DP = D / OH;
   constexpr int OSTG = 32 * DP * 4;
-  constexpr int LDS_BYTES = kWaves * OSTG > 2 * STAGE ? kWaves * OSTG : 2 * STAGE;
+  constexpr int RING = STAG ? 2 * KT + 3 * VT : 2 * STAGE;
+  constexpr int LDS_BYTES = kWaves * OSTG > RING ? kWaves * OSTG : RING;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -736,8 +746,16 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
     f32x16 sa[NKB], sb[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sa[kb] = sb[kb] = f32x16{};   // row_max reads sb once unused
-    if (ntiles > 0) { issue_k(0, KST[0]); issue_v(0, VST[0]); }
-    if (ntiles > 1) issue_k(1, KST[1]);
+    // Staggered teams (STAG): the trailing team (hp = 1) meets the leading
+    // team's end-of-tile barrier between its exponentials and its P.V, so it
+    // runs P.V(t) while the leading team computes S(t+2) and P(t+1). K(t+2)
+    // then overwrites K(t) only after both teams' S(t+1) (before that
+    // barrier), and V(t) needs a third stage: the trailing team still reads
+    // it while V(t+1) arrives and V(t+2) is issued.
+    const bool lead = !STAG || hp == 0;
+    auto vst_of = [&](int t) -> unsigned { return STAG ? 2 * KT + (t % 3) * VT : VST[t & 1]; };
+    if (lead && ntiles > 0) { issue_k(0, KST[0]); issue_v(0, vst_of(0)); }
+    if (lead && ntiles > 1) issue_k(1, KST[1]);
     load_q();
     dma_wait();
     __syncthreads();
@@ -752,7 +770,7 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
 
     auto iter = [&](int t, auto parity, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
       constexpr int P = decltype(parity)::value;
-      if (t + 2 < ntiles) issue_k(t + 2, KST[P]);
+      if (lead && t + 2 < ntiles) issue_k(t + 2, KST[P]);
       if constexpr (XMAX) base = rebase(tm);
       u32x4 pk[NKS];
       float ts;
@@ -781,14 +799,15 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
       }
       if constexpr (!XMAX) sum_check(cur, base, ts, pk);
       l += ts;
+      if (STAG && !lead) __syncthreads();   // the trailing team's barrier (see above)
       // V(t+1) goes out here rather than with K(t+2): its stage held V(t-1),
       // long consumed, and issuing it mid-tile spreads the DMA over the tile.
-      if (t + 1 < ntiles) issue_v(t + 1, VST[1 - P]);
+      if (lead && t + 1 < ntiles) issue_v(t + 1, vst_of(t + 1));
       // P.V of tile t with the row max of tile t+1 interleaved (its base moves
       // at the top of the next step, after this P.V, as before); a straddling
       // tile t+1 is masked first. After the last tile the max is unused.
       if (t + 1 < ntiles && needs_mask(tile(t + 1) * BN)) apply_mask(nxt, tile(t + 1) * BN);
-      pv(lds + VST[P], pk);
+      pv(lds + (STAG ? vst_of(t) : VST[P]), pk);
       if constexpr (XMAX) tm = row_max(nxt);
       {
         // P.V: V^T operand reads four MFMAs ahead; the max's VALU among them.
@@ -802,13 +821,19 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
           if constexpr (XMAX) __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
         }
       }
-      dma_wait();        // this wave's part of K(t+2), V(t+1) has landed
-      __syncthreads();   // ... everywhere; K(t+1) and V(t) may be overwritten next
+      if (lead) {
+        dma_wait();        // this wave's part of K(t+2), V(t+1) has landed
+        __syncthreads();   // ... everywhere; K(t+1) and V(t) may be overwritten next
+      }
     };
     for (int t = 0; t < ntiles; t += 2) {
       iter(t, std::integral_constant<int, 0>{}, sa, sb);
       if (t + 1 < ntiles) iter(t + 1, std::integral_constant<int, 1>{}, sb, sa);
     }
+    // Every wave meets the same number of barriers: two before the loop, one
+    // per tile, and (staggered) this one, after which the trailing team's last
+    // P.V is done with the LDS that the O staging reuses.
+    if constexpr (STAG) __syncthreads();
   } else {
     // Plain double buffer: tile t+1 (K and V^T together) arrives while tile t
     // is computed from the other stage.
