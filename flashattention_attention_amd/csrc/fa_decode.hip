@@ -530,14 +530,20 @@ __device__ __forceinline__ void split_run(const DecodeArgs& a, int b, int h0, in
     split_attend<D, G, BF16>(a, b, h0, lo, hi, lane, m, l, o);
 }
 
-// Launch order of the decode work-groups. A "cluster" is the work-groups that
-// read the same K/V rows: one sequence, one KV head, one split (or group of
-// splits), and the q_per_kv head groups of that KV head. Work-group i runs on
-// XCD i % 8, which has its own L2: a cluster's work-groups all go to one XCD,
-// so after the first fetch its rows come from that L2 (the loads are
-// non-temporal but reach L2), and consecutive clusters, KV heads fastest
-// (the same token rows), go to consecutive XCDs. With one head group per KV
-// head this is the plain (KV head, split, sequence) order.
+// Launch order of the decode work-groups. A "unit" is one (sequence, split)
+// pair with work (or split group, for the fused kernel), numbered densely in
+// (sequence, split) order; a "cluster" is the work-groups that read the same
+// K/V rows: one unit, one KV head, and the q_per_kv head groups of that KV
+// head. Work-group i runs on XCD i % 8, which has its own L2: a cluster's
+// work-groups all go to one XCD, so after the first fetch its rows come from
+// that L2 (the loads are non-temporal but reach L2), and consecutive clusters,
+// KV heads fastest (the same token rows), go to consecutive XCDs. The grid is
+// sized for every sequence at the longest one's split count, but the units
+// are numbered densely, so every work-group with work comes before every one
+// without (those exit at once). Work-groups are dispatched in order, each as
+// soon as a slot frees: with the empty ones interleaved among the real ones,
+// the real ones landed unevenly on the compute units and some waited behind a
+// full one while others sat idle.
 struct DecItem {
   int b, hg, y;   // sequence, head group, split (or split group)
   bool valid;
@@ -546,17 +552,53 @@ __host__ __device__ inline int64_t dec_grid(int batch, int n_heads_kv, int q_per
   const int64_t c = (int64_t)batch * n_heads_kv * ny;
   return 8 * ((c + 7) / 8) * q_per_kv;
 }
-__device__ inline DecItem dec_item(int id, int batch, int n_heads_kv, int q_per_kv, int ny) {
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ int wave_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+// Work-group id's item; units_of(L) is the number of units of a sequence of L
+// keys. Every lane of the wave takes part; the result is wave-uniform.
+template <typename UnitsOf>
+__device__ inline DecItem dec_item(int id, const int* kv_lens, int batch, int n_heads_kv,
+                                   int q_per_kv, int lane, UnitsOf units_of) {
   const int x = id & 7, m = id >> 3;
   const int j = m % q_per_kv;
   const int64_t c = (int64_t)(m / q_per_kv) * 8 + x;
-  DecItem it;
-  it.valid = c < (int64_t)batch * n_heads_kv * ny;
   const int hk = (int)(c % n_heads_kv);
-  const int64_t r = c / n_heads_kv;
-  it.y = (int)(r % ny);
-  it.b = (int)(r / ny);
+  const int64_t r = c / n_heads_kv;          // unit
+  DecItem it;
+  it.valid = false;
+  it.b = it.y = 0;
   it.hg = hk * q_per_kv + j;
+  int64_t base = 0;                          // units of the sequences before b0
+  for (int b0 = 0; b0 < batch; b0 += 256) {
+    int n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {            // the four loads in flight together
+      const int b = b0 + 64 * i + lane;
+      n[i] = b < batch ? units_of(kv_lens[b]) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int incl = wave_scan(n[i], lane);
+      const uint64_t hit = __ballot(base + incl > r);
+      if (hit) {
+        const int first = __ffsll((long long)hit) - 1;
+        it.b = b0 + 64 * i + first;
+        it.y = (int)(r - base - __shfl(incl - n[i], first));
+        it.b = __builtin_amdgcn_readfirstlane(it.b);
+        it.y = __builtin_amdgcn_readfirstlane(it.y);
+        it.valid = true;
+        return it;
+      }
+      base += __shfl(incl, 63);
+    }
+  }
   return it;
 }
 
@@ -569,12 +611,13 @@ decode_partial_kernel(DecodeArgs a) {
   constexpr int EPL = D / LPK;
   const int lane = threadIdx.x;
   const int qpk = a.n_heads_q / a.n_heads_kv / G;   // head groups per KV head
-  const DecItem it = dec_item(blockIdx.x, a.batch, a.n_heads_kv, qpk, a.max_splits);
-  if (!it.valid) return;
+  const int sl = a.split_len, ms = a.max_splits;
+  const DecItem it = dec_item(blockIdx.x, a.kv_lens, a.batch, a.n_heads_kv, qpk, lane,
+                              [=](int L) { return L < 1 ? 0 : min((L + sl - 1) / sl, ms); });
+  if (!it.valid) return;                 // no unit: nothing read or written
   const int h0 = it.hg * G, s = it.y, b = it.b;
   const int L = a.kv_lens[b];
   const int lo = s * a.split_len;
-  if (L < 1 || lo >= L) return;          // empty split: nothing read or written
   const int hi = min(L, lo + a.split_len);
   const int slot = lane / LPK;
   const int c = lane % LPK;
@@ -733,7 +776,14 @@ decode_fused_kernel(DecodeArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qpk = a.n_heads_q / a.n_heads_kv / G;   // head groups per KV head
-  const DecItem it = dec_item(blockIdx.x, a.batch, a.n_heads_kv, qpk, a.max_wg);
+  // A sequence with no key or more splits than max_splits has one unit (its
+  // work-group writes the NaN mark), else one per group of NW splits.
+  const int slen = a.split_len, ms = a.max_splits;
+  const DecItem it = dec_item(blockIdx.x, a.kv_lens, a.batch, a.n_heads_kv, qpk, lane,
+                              [=](int L) {
+                                const int n = L < 1 ? 0 : (L + slen - 1) / slen;
+                                return n < 1 || n > ms ? 1 : (n + NW - 1) / NW;
+                              });
   if (!it.valid) return;
   const int hg = it.hg, h0 = hg * G, y = it.y, b = it.b;
   const int L = a.kv_lens[b];
@@ -810,7 +860,7 @@ decode_fused_kernel(DecodeArgs a) {
   __syncthreads();
   if (tid == 0)
     is_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              a.max_wg - 1;
+              (bad ? 0 : nwg - 1);
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // drop stale cached partials
