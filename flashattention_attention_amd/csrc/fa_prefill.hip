@@ -274,8 +274,23 @@ __host__ __device__ inline bool wg_serial_fits(int groups, int per_group, int nq
 
 // per_group: work units (sets of query heads) per group. serial_slots > 0:
 // the serial order for that many work-group slots per XCD.
+//
+// rot_cus > 0 (two work-groups per compute unit, rot_cus compute units per
+// XCD, a grid of at least two such rounds): the first work-groups of a launch
+// land in a fixed pattern, position j of an XCD's sequence (id >> 3) on that
+// XCD's compute unit j % rot_cus for j < 2 * rot_cus, so a compute unit's two
+// first work-groups are positions j and j + rot_cus. In longest-first order
+// that pairs the k-th longest block of each half, and the compute units
+// holding the two longest pairs finish last while others idle. The second
+// half of those positions is rotated by 5/16 of rot_cus (the ids stay a
+// permutation of the same set), which decouples the two.
 __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int per_group,
-                                          int nqb, int serial_slots = 0) {
+                                          int nqb, int serial_slots = 0, int rot_cus = 0) {
+  if (rot_cus > 0) {
+    const int j = id >> 3;
+    if (j >= rot_cus && j < 2 * rot_cus)
+      id = ((rot_cus + (j - rot_cus + (rot_cus * 5) / 16) % rot_cus) << 3) | (id & 7);
+  }
   const int groups = batch * n_heads_kv;
   int g, u, rank;                                    // rank 0 = longest block
   bool valid = true, rev = false;
@@ -402,7 +417,8 @@ prefill_kernel(PrefillArgs a, const unsigned short* __restrict__ vt_ws,
   const int per_group = a.n_heads_q / a.n_heads_kv;
   int nunits = nqb;
   if constexpr (SPLIT) nunits = sp.n_units;
-  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nunits, a.wg_serial);
+  const WgItem item = wg_item(blockIdx.x, a.batch, a.n_heads_kv, per_group / HP, nunits, a.wg_serial,
+                              a.wg_rot);
   if (!item.valid) return;
   int qb = item.qb, half = -1;   // half: -1 whole block, else which half of its key tiles
   if constexpr (SPLIT) {
@@ -1308,6 +1324,13 @@ hipError_t launch_pack_d(const PrefillArgs& a, const VtArgs& w, hipStream_t stre
   return hipGetLastError();
 }
 
+// wg_item's rotation for a launch of two work-groups per compute unit (32
+// compute units per XCD): on when the grid fills both first rounds.
+inline int first_round_rotation(unsigned grid) {
+  constexpr int kCusPerXcd = 32;
+  return grid >= 2u * kCusPerXcd * 8 ? kCusPerXcd : 0;
+}
+
 template <int D, bool BF16>
 hipError_t launch_attn_d(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hipStream_t stream) {
   constexpr int BM = block_rows(D);
@@ -1324,6 +1347,7 @@ hipError_t launch_attn_d(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hi
     constexpr int HP = decltype(hp_c)::value;
     constexpr bool TRIO = decltype(trio_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
+    a.wg_rot = HP == 1 && !TRIO && a.wg_serial == 0 ? first_round_rotation(grid.x) : 0;
     if (xmax)
       hipLaunchKernelGGL((prefill_kernel<D, BF16, true, HP, false, false, TRIO>), grid,
                          dim3(64 * wg_waves(D, HP)), 0, stream, a, (const unsigned short*)w.ws,
@@ -1363,6 +1387,7 @@ hipError_t launch_attn_vrow_d(const PrefillArgs& a0, bool unnorm, hipStream_t st
   const auto go = [&](auto hp_c) {
     constexpr int HP = decltype(hp_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
+    a.wg_rot = HP == 1 ? first_round_rotation(grid.x) : 0;
     if (xmax)
       hipLaunchKernelGGL((prefill_kernel<D, false, true, HP, false, true>), grid,
                          dim3(64 * wg_waves(D, HP)), 0, stream, a, nullptr, NoSplit{});
