@@ -37,7 +37,7 @@ struct PrefillArgs {
   int window;              // > 0: key j visible only if j > q_pos - window
   const float* sink_logits;  // device [n_heads_q] per-head sink logit, or null
   int wg_serial;           // serial work-group order: work-group slots per XCD (0 = off; set by the launcher)
-  int wg_rot;              // rotated second round of first-dispatched work-groups: compute units per XCD (0 = off; set by the launcher)
+  int wg_rot;              // second round of first-dispatched work-groups rotated (reversed in the serial order): compute units per XCD (0 = off; set by the launcher)
   int unnorm;              // un-normalized O (set by the launcher)
 };
 

@@ -283,10 +283,13 @@ __host__ __device__ inline bool wg_serial_fits(int groups, int per_group, int nq
 // that pairs the k-th longest block of each half, and the compute units
 // holding the two longest pairs finish last while others idle. The second
 // half of those positions is rotated by 5/16 of rot_cus (the ids stay a
-// permutation of the same set), which decouples the two.
+// permutation of the same set), which decouples the two. In the serial order
+// (whose first round is one group's blocks, longest first, followed by whole
+// further groups) the second half of the first round is reversed instead, so
+// that each compute unit starts with a long and a short block of that group.
 __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int per_group,
                                           int nqb, int serial_slots = 0, int rot_cus = 0) {
-  if (rot_cus > 0) {
+  if (rot_cus > 0 && serial_slots == 0) {
     const int j = id >> 3;
     if (j >= rot_cus && j < 2 * rot_cus)
       id = ((rot_cus + (j - rot_cus + (rot_cus * 5) / 16) % rot_cus) << 3) | (id & 7);
@@ -295,7 +298,8 @@ __host__ __device__ inline WgItem wg_item(int id, int batch, int n_heads_kv, int
   int g, u, rank;                                    // rank 0 = longest block
   bool valid = true, rev = false;
   if (serial_slots > 0 && groups % 8 == 0) {
-    const int x = id & 7, j = id >> 3;
+    const int x = id & 7, j0 = id >> 3;
+    const int j = rot_cus > 0 && j0 >= rot_cus && j0 < 2 * rot_cus ? 3 * rot_cus - 1 - j0 : j0;
     const int per_g = per_group * nqb;
     const int gi = j / per_g;                        // this XCD's gi-th group
     const int r = j - gi * per_g;
@@ -1324,8 +1328,9 @@ hipError_t launch_pack_d(const PrefillArgs& a, const VtArgs& w, hipStream_t stre
   return hipGetLastError();
 }
 
-// wg_item's rotation for a launch of two work-groups per compute unit (32
-// compute units per XCD): on when the grid fills both first rounds.
+// wg_item's first-round rotation (or, in the serial order, reversal) for a
+// launch of two work-groups per compute unit (32 compute units per XCD): on
+// when the grid fills both first rounds.
 inline int first_round_rotation(unsigned grid) {
   constexpr int kCusPerXcd = 32;
   return grid >= 2u * kCusPerXcd * 8 ? kCusPerXcd : 0;
@@ -1347,7 +1352,7 @@ hipError_t launch_attn_d(const PrefillArgs& a0, const VtArgs& w, bool unnorm, hi
     constexpr int HP = decltype(hp_c)::value;
     constexpr bool TRIO = decltype(trio_c)::value;
     const dim3 grid(wg_count(a.batch * a.n_heads_kv, per_group / HP, nqb));
-    a.wg_rot = HP == 1 && !TRIO && a.wg_serial == 0 ? first_round_rotation(grid.x) : 0;
+    a.wg_rot = HP == 1 && !TRIO ? first_round_rotation(grid.x) : 0;
     if (xmax)
       hipLaunchKernelGGL((prefill_kernel<D, BF16, true, HP, false, false, TRIO>), grid,
                          dim3(64 * wg_waves(D, HP)), 0, stream, a, (const unsigned short*)w.ws,
