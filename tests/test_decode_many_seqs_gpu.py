@@ -1,4 +1,4 @@
-"""Decode over batches of many sequences (80, 130 and 300) against the fp64
+"""Decode over batches of many sequences (70, 80, 130 and 300) against the fp64
 oracle (needs an MI355X).
 
 Source: "66 · D2: explicit K+V register staging ...", section 1 (split-KV
@@ -55,6 +55,7 @@ CASES = [
     (300, 8, 2, 128, "f16", 32, 5),
     (80, 28, 4, 128, "bf16", 16, 6),
     (130, 4, 4, 64, "f16", 16, 4),
+    (70, 16, 2, 256, "bf16", 32, 4),     # head_dim 256: the VALU split form
 ]
 
 
